@@ -1,0 +1,297 @@
+"""Python binding of libslm, the MI355X (gfx950) attention hot path of a
+bounded-generation small-language-model engine.
+
+This module only marshals arguments: it checks torch tensors (device, dtype,
+contiguity), passes their device pointers and the current HIP stream to the
+C ABI declared in ``include/slm.h``, and raises on a non-OK status.  Every
+step of the computation runs in the HIP kernels of ``libslm.so``; there is no
+CPU or PyTorch fallback, and importing this module fails loudly when the
+library has not been built (``python -m bounded_generation_slm_amd._build``).
+
+The functions carry the C names (``slm_packed_prefill_attn`` and so on) and
+take a :class:`Context` first; the same calls are available as methods.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libslm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libslm.so is not built; run `python -m bounded_generation_slm_amd._build` "
+        "(hipcc, gfx950) -- there is no fallback implementation")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+SLM_OK, SLM_ERR_INVALID_ARG, SLM_ERR_UNSUPPORTED, SLM_ERR_CAPACITY = 0, 1, 2, 3
+SLM_ERR_ALIAS, SLM_ERR_DEVICE, SLM_ERR_OOM = 4, 5, 6
+SLM_BF16, SLM_F32 = 0, 1
+
+EXPORTED = (
+    "slm_abi_version", "slm_status_string", "slm_ctx_create", "slm_ctx_destroy",
+    "slm_ctx_set_stream", "slm_ctx_check", "slm_ctx_last_error", "slm_packed_prefill_attn",
+    "slm_gather_last", "slm_beam_decode_attn", "slm_beam_topk_merge", "slm_beam_reorder_suffix",
+)
+
+
+class _Caps(ctypes.Structure):
+    _fields_ = [("max_requests", ctypes.c_int32), ("max_beams", ctypes.c_int32),
+                ("max_vocab", ctypes.c_int32)]
+
+
+class _BeamAttnArgs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_layers", "num_requests", "width", "prompt_len", "hist_len", "suffix_cap",
+        "n_heads_q", "n_heads_kv", "head_dim")] + [("scale", ctypes.c_float)] + [
+        (n, ctypes.c_void_p) for n in (
+            "q", "prefix_k", "prefix_v", "suffix_k_in", "suffix_v_in", "k_new", "v_new", "parent",
+            "suffix_k_out", "suffix_v_out", "out")] + [("out_dtype", ctypes.c_int)]
+
+
+_P, _I, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+_lib.slm_abi_version.restype = ctypes.c_int
+_lib.slm_status_string.restype = ctypes.c_char_p
+_lib.slm_status_string.argtypes = [ctypes.c_int]
+_lib.slm_ctx_create.argtypes = [ctypes.c_int, ctypes.POINTER(_Caps), ctypes.POINTER(_P)]
+_lib.slm_ctx_destroy.argtypes = [_P]
+_lib.slm_ctx_destroy.restype = None
+_lib.slm_ctx_set_stream.argtypes = [_P, _P]
+_lib.slm_ctx_check.argtypes = [_P]
+_lib.slm_ctx_last_error.argtypes = [_P]
+_lib.slm_ctx_last_error.restype = ctypes.c_char_p
+_lib.slm_packed_prefill_attn.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, ctypes.c_int]
+_lib.slm_gather_last.argtypes = [_P, _P, _P, _I, _I, _I, ctypes.c_int, _P]
+_lib.slm_beam_decode_attn.argtypes = [_P, ctypes.POINTER(_BeamAttnArgs)]
+_lib.slm_beam_topk_merge.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]
+_lib.slm_beam_reorder_suffix.argtypes = [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
+for _name in ("slm_ctx_create", "slm_ctx_set_stream", "slm_ctx_check", "slm_packed_prefill_attn",
+              "slm_gather_last", "slm_beam_decode_attn", "slm_beam_topk_merge", "slm_beam_reorder_suffix"):
+    getattr(_lib, _name).restype = ctypes.c_int
+
+
+class SlmError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__("%s: %s" % (_lib.slm_status_string(status).decode(), detail))
+
+
+def abi_version() -> int:
+    return _lib.slm_abi_version()
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtypes, device) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s: dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if t.device != device:
+        raise ValueError("%s is on %s, the context is on %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+_BF16 = (torch.bfloat16, torch.int16)
+_OUT = {torch.float32: SLM_F32, torch.bfloat16: SLM_BF16}
+
+
+class Context:
+    """A libslm context on one GPU: its stream is torch's current stream at
+    each call, and its workspace is sized by the caps at creation.
+
+    ``device=-1`` makes a dry-run context: every call runs the library's
+    host-side validation on CPU tensors and launches nothing."""
+
+    def __init__(self, device: int = 0, max_requests: int = 64, max_beams: int = 512,
+                 max_vocab: int = 262144):
+        self.dry_run = device < 0
+        if self.dry_run:
+            self.device = torch.device("cpu")
+        else:
+            self.device = torch.device("cuda", device)
+            torch.cuda.init()
+        caps = _Caps(max_requests, max_beams, max_vocab)
+        handle = _P()
+        rc = _lib.slm_ctx_create(device, ctypes.byref(caps), ctypes.byref(handle))
+        if rc != SLM_OK:
+            raise SlmError(rc, "slm_ctx_create(device=%d)" % device)
+        self._h = handle
+        self.caps = dict(max_requests=max_requests, max_beams=max_beams, max_vocab=max_vocab)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.slm_ctx_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _stream(self):
+        if self.dry_run:
+            return
+        s = torch.cuda.current_stream(self.device).cuda_stream
+        _lib.slm_ctx_set_stream(self._h, _P(s))
+
+    def _raise(self, rc: int, what: str):
+        if rc != SLM_OK:
+            raise SlmError(rc, "%s: %s" % (what, _lib.slm_ctx_last_error(self._h).decode()))
+
+    def check(self):
+        """Synchronise the stream and raise if a kernel flagged bad device-side
+        arguments (cu_seqlens, parent)."""
+        self._stream()
+        self._raise(_lib.slm_ctx_check(self._h), "slm_ctx_check")
+
+    # -- calls (argument marshalling only) --
+    def packed_prefill_attn(self, q, k, v, cu_seqlens, max_seqlen: int, scale: Optional[float] = None,
+                            out: Optional[torch.Tensor] = None, out_dtype=torch.float32):
+        return slm_packed_prefill_attn(self, q, k, v, cu_seqlens, max_seqlen, scale, out, out_dtype)
+
+    def gather_last(self, hidden, cu_seqlens, out=None):
+        return slm_gather_last(self, hidden, cu_seqlens, out)
+
+    def beam_decode_attn(self, *args, **kw):
+        return slm_beam_decode_attn(self, *args, **kw)
+
+    def beam_topk_merge(self, logprobs, cum, width: int, tokens=None, parent=None, cum_out=None):
+        return slm_beam_topk_merge(self, logprobs, cum, width, tokens, parent, cum_out)
+
+    def beam_reorder_suffix(self, parent, k_in, v_in, rows: int, k_out, v_out):
+        return slm_beam_reorder_suffix(self, parent, k_in, v_in, rows, k_out, v_out)
+
+
+def slm_packed_prefill_attn(ctx: Context, q, k, v, cu_seqlens, max_seqlen: int,
+                            scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                            out_dtype=torch.float32) -> torch.Tensor:
+    """q [T,Hq,D], k/v [T,Hkv,D] bf16; cu_seqlens [B+1] int32 (device).
+    Returns out [T,Hq,D] (float32 or bfloat16)."""
+    dev = ctx.device
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (T, Hkv, D) or v.shape != (T, Hkv, D):
+        raise ValueError("k and v must be [T, Hkv, D] matching q")
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=out_dtype, device=dev)
+    if out.shape != (T, Hq, D) or out.dtype not in _OUT:
+        raise ValueError("out must be [T, Hq, D] float32 or bfloat16")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    ctx._stream()
+    rc = _lib.slm_packed_prefill_attn(
+        ctx._h, _ptr(q, "q", _BF16, dev), _ptr(k, "k", _BF16, dev), _ptr(v, "v", _BF16, dev),
+        _ptr(cu_seqlens, "cu_seqlens", (torch.int32,), dev), cu_seqlens.numel() - 1, T,
+        int(max_seqlen), Hq, Hkv, D, scale, _ptr(out, "out", tuple(_OUT), dev), _OUT[out.dtype])
+    ctx._raise(rc, "slm_packed_prefill_attn")
+    return out
+
+
+def slm_gather_last(ctx: Context, hidden, cu_seqlens, out=None) -> torch.Tensor:
+    """hidden [T,H] (bf16 or fp32) -> out [B,H], the last valid row of each sequence."""
+    dev = ctx.device
+    T, H = hidden.shape
+    B = cu_seqlens.numel() - 1
+    dt = {torch.bfloat16: SLM_BF16, torch.float32: SLM_F32}.get(hidden.dtype)
+    if dt is None:
+        raise TypeError("hidden must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty((B, H), dtype=hidden.dtype, device=dev)
+    if out.shape != (B, H) or out.dtype != hidden.dtype:
+        raise ValueError("out must be [B, H] of hidden's dtype")
+    ctx._stream()
+    rc = _lib.slm_gather_last(ctx._h, _ptr(hidden, "hidden", (hidden.dtype,), dev),
+                              _ptr(cu_seqlens, "cu_seqlens", (torch.int32,), dev), B, T, H, dt,
+                              _ptr(out, "out", (hidden.dtype,), dev))
+    ctx._raise(rc, "slm_gather_last")
+    return out
+
+
+def slm_beam_decode_attn(ctx: Context, q, prefix_k, prefix_v, suffix_k_in, suffix_v_in, k_new, v_new,
+                         parent, hist_len: int, suffix_k_out, suffix_v_out, out=None,
+                         scale: Optional[float] = None, out_dtype=torch.float32) -> torch.Tensor:
+    """One decode step over all layers.  q [NL,R,W,Hq,D]; prefix_k/v
+    [NL,R,P,Hkv,D]; suffix_*_in/out [NL,R,W,S_cap,Hkv,D]; k_new/v_new
+    [NL,R,W,Hkv,D]; parent [R,W] int32 or None.  Returns out [NL,R,W,Hq,D]."""
+    dev = ctx.device
+    NL, R, W, Hq, D = q.shape
+    P, Hkv = prefix_k.shape[2], prefix_k.shape[3]
+    S_cap = suffix_k_out.shape[3]
+    if prefix_k.shape != (NL, R, P, Hkv, D) or prefix_v.shape != prefix_k.shape:
+        raise ValueError("prefix_k/v must be [NL,R,P,Hkv,D]")
+    if k_new.shape != (NL, R, W, Hkv, D) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [NL,R,W,Hkv,D]")
+    sshape = (NL, R, W, S_cap, Hkv, D)
+    for name, t in (("suffix_k_out", suffix_k_out), ("suffix_v_out", suffix_v_out),
+                    ("suffix_k_in", suffix_k_in), ("suffix_v_in", suffix_v_in)):
+        if t is not None and tuple(t.shape) != sshape:
+            raise ValueError("%s must be %s" % (name, sshape))
+    if parent is not None and tuple(parent.shape) != (R, W):
+        raise ValueError("parent must be [R, W]")
+    if out is None:
+        out = torch.empty((NL, R, W, Hq, D), dtype=out_dtype, device=dev)
+    if tuple(out.shape) != (NL, R, W, Hq, D) or out.dtype not in _OUT:
+        raise ValueError("out must be [NL,R,W,Hq,D] float32 or bfloat16")
+    a = _BeamAttnArgs()
+    a.n_layers, a.num_requests, a.width, a.prompt_len = NL, R, W, P
+    a.hist_len, a.suffix_cap, a.n_heads_q, a.n_heads_kv, a.head_dim = int(hist_len), S_cap, Hq, Hkv, D
+    a.scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    a.q = _ptr(q, "q", _BF16, dev)
+    a.prefix_k, a.prefix_v = _ptr(prefix_k, "prefix_k", _BF16, dev), _ptr(prefix_v, "prefix_v", _BF16, dev)
+    a.suffix_k_in = _ptr(suffix_k_in, "suffix_k_in", _BF16, dev)
+    a.suffix_v_in = _ptr(suffix_v_in, "suffix_v_in", _BF16, dev)
+    a.k_new, a.v_new = _ptr(k_new, "k_new", _BF16, dev), _ptr(v_new, "v_new", _BF16, dev)
+    a.parent = _ptr(parent, "parent", (torch.int32,), dev)
+    a.suffix_k_out = _ptr(suffix_k_out, "suffix_k_out", _BF16, dev)
+    a.suffix_v_out = _ptr(suffix_v_out, "suffix_v_out", _BF16, dev)
+    a.out, a.out_dtype = _ptr(out, "out", tuple(_OUT), dev), _OUT[out.dtype]
+    ctx._stream()
+    ctx._raise(_lib.slm_beam_decode_attn(ctx._h, ctypes.byref(a)), "slm_beam_decode_attn")
+    return out
+
+
+def slm_beam_topk_merge(ctx: Context, logprobs, cum, width: int, tokens=None, parent=None, cum_out=None):
+    """logprobs [R,Win,V] fp32, cum [R,Win] fp32 -> (tokens, parent, cum_out), each [R,W]."""
+    dev = ctx.device
+    R, Win, V = logprobs.shape
+    if tuple(cum.shape) != (R, Win):
+        raise ValueError("cum must be [R, Win]")
+    W = int(width)
+    tokens = torch.empty((R, W), dtype=torch.int32, device=dev) if tokens is None else tokens
+    parent = torch.empty((R, W), dtype=torch.int32, device=dev) if parent is None else parent
+    cum_out = torch.empty((R, W), dtype=torch.float32, device=dev) if cum_out is None else cum_out
+    for name, t in (("tokens", tokens), ("parent", parent), ("cum_out", cum_out)):
+        if tuple(t.shape) != (R, W):
+            raise ValueError("%s must be [R, W]" % name)
+    ctx._stream()
+    rc = _lib.slm_beam_topk_merge(
+        ctx._h, _ptr(logprobs, "logprobs", (torch.float32,), dev), _ptr(cum, "cum", (torch.float32,), dev),
+        R, Win, V, W, _ptr(tokens, "tokens", (torch.int32,), dev), _ptr(parent, "parent", (torch.int32,), dev),
+        _ptr(cum_out, "cum_out", (torch.float32,), dev))
+    ctx._raise(rc, "slm_beam_topk_merge")
+    return tokens, parent, cum_out
+
+
+def slm_beam_reorder_suffix(ctx: Context, parent, k_in, v_in, rows: int, k_out, v_out):
+    """k_out[l,r,j,i] = k_in[l,r,parent[r,j],i] for i < rows (and V)."""
+    dev = ctx.device
+    NL, R, W, S_cap, Hkv, D = k_in.shape
+    for name, t in (("v_in", v_in), ("k_out", k_out), ("v_out", v_out)):
+        if t.shape != k_in.shape:
+            raise ValueError("%s must match k_in's shape" % name)
+    ctx._stream()
+    rc = _lib.slm_beam_reorder_suffix(
+        ctx._h, NL, R, W, int(rows), S_cap, Hkv, D, _ptr(parent, "parent", (torch.int32,), dev),
+        _ptr(k_in, "k_in", _BF16, dev), _ptr(v_in, "v_in", _BF16, dev), _ptr(k_out, "k_out", _BF16, dev),
+        _ptr(v_out, "v_out", _BF16, dev))
+    ctx._raise(rc, "slm_beam_reorder_suffix")
+    return k_out, v_out

@@ -1,0 +1,325 @@
+// Fixed-step beam-search decode attention for gfx950: one shared prompt K/V
+// per request, one short suffix K/V per beam.
+//
+// Operation (page "SLM 生成式高并发推理引擎：延迟约束下的有效吞吐优化", §1.2: the
+// beams of one request share one prompt K/V and each keeps a short suffix
+// K/V; §1.1: beams carry parent indices across steps).  For beam j and query
+// head h the keys are the P prompt rows of its request, the history rows of
+// its parent beam and its own new row, all visible.
+//
+// Work decomposition: a workgroup (8 waves) owns one (layer, request, KV
+// head, chunk of query rows).  The query rows of a (layer, request, KV head)
+// are the W beams x G query heads of the group, stacked in the MFMA M
+// dimension (row m = beam * G + head-in-group).  The prompt K and V^T of the
+// unit are staged in LDS once per workgroup and reused by every 32-row block,
+// so prompt K/V bytes come from HBM once per request instead of once per beam.
+// Each wave runs S^T = K Q^T and O^T += V^T P^T on the prompt (as in packed
+// prefill, online softmax in registers), then folds in the beam's own suffix
+// keys with vector dot products.  The workgroup also writes the suffix in the
+// current beam order (parent's history rows + the new row), so the reorder
+// after the previous merge costs no separate pass.
+#include "common.h"
+#include "kernels.h"
+
+namespace slm {
+namespace {
+
+constexpr int kDecThreads = 512;
+
+template <int D>
+struct DecodeLds {
+    static constexpr int KROW = D + 8;
+    static __host__ __device__ int p_pad(int P) { return (P + 63) / 64 * 64; }
+    static __host__ __device__ int vrow(int P) { return p_pad(P) + 8; }
+    static __host__ __device__ size_t bytes(int P) {
+        return ((size_t)p_pad(P) * KROW + (size_t)D * vrow(P)) * sizeof(uint16_t);
+    }
+};
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(kDecThreads, 1) void beam_decode_attn_kernel(const DecodeParams p,
+                                                                          int chunks, int chunk_rows) {
+    constexpr int NKS = D / 16, NDB = D / 32, KROW = D + 8;
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    const int P = p.prompt_len;
+    const int PP = DecodeLds<D>::p_pad(P);
+    const int VROW = DecodeLds<D>::vrow(P);
+    uint16_t* k_lds = lds;                        // [PP][KROW]
+    uint16_t* vt_lds = lds + (size_t)PP * KROW;   // [D][VROW], keys permuted per 16
+
+    const int R = p.num_requests, W = p.width, G = p.group, Hkv = p.n_heads_kv;
+    const int n_units = p.n_layers * R * Hkv;
+    const int idx = blockIdx.x;
+    const int xcd = idx % kNumXcd, slot = idx / kNumXcd;
+    const int unit = (slot / chunks) * kNumXcd + xcd;
+    const int chunk = slot % chunks;
+    if (unit >= n_units) return;
+    const int g = unit % Hkv;
+    const int lr = unit / Hkv;                    // l * R + r
+    const int r = lr % R;
+    const int M = W * G;
+    const int row0 = chunk * chunk_rows;
+    if (row0 >= M) return;
+    const int row1 = min(M, row0 + chunk_rows);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, hf = lane >> 5;
+    const int64_t kv_row = (int64_t)Hkv * D;      // elements between consecutive rows
+
+    // ---- stage prompt K and V^T of (l, r, g) into LDS ----
+    {
+        const uint16_t* pk = p.prefix_k + (int64_t)lr * P * kv_row + (int64_t)g * D;
+        const uint16_t* pv = p.prefix_v + (int64_t)lr * P * kv_row + (int64_t)g * D;
+        const int kchunks = PP * (D / 8);
+        for (int c = tid; c < kchunks; c += kDecThreads) {
+            const int key = c / (D / 8), dg = c % (D / 8);
+            const u32x4 x = key < P ? *(const u32x4*)(pk + key * kv_row + dg * 8) : u32x4{0u, 0u, 0u, 0u};
+            *(u32x4*)(k_lds + key * KROW + dg * 8) = x;
+        }
+        // V^T: unit = (16-key chunk c16, half vh, d-group dg); keys 16c16 + 8(e/4) + 4vh + e%4
+        const int vunits = (PP / 16) * 2 * (D / 8);
+        for (int u = tid; u < vunits; u += kDecThreads) {
+            const int c8 = u % ((PP / 16) * 2), dg = u / ((PP / 16) * 2);
+            const int c16 = c8 >> 1, vh = c8 & 1;
+            u32x4 vb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int key = 16 * c16 + 8 * (e >> 2) + 4 * vh + (e & 3);
+                vb[e] = key < P ? *(const u32x4*)(pv + key * kv_row + dg * 8) : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int dd = 0; dd < 8; ++dd) {
+                u32x4 t;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t a = vb[2 * w][dd >> 1], c = vb[2 * w + 1][dd >> 1];
+                    t[w] = (dd & 1) ? ((a >> 16) | (c & 0xFFFF0000u)) : ((a & 0xFFFFu) | (c << 16));
+                }
+                *(u32x4*)(vt_lds + (dg * 8 + dd) * VROW + 16 * c16 + 8 * vh) = t;
+            }
+        }
+    }
+
+    // ---- suffix in the current order for the beams whose first row is here ----
+    {
+        const int wb0 = (row0 + G - 1) / G, wb1 = (row1 + G - 1) / G;   // beams with w*G in [row0,row1)
+        const int rows_out = p.hist_len + 1;
+        const int cpr = D / 8;                                          // 16-byte chunks per row
+        const int total = (wb1 - wb0) * rows_out * cpr;
+        for (int c = tid; c < total; c += kDecThreads) {
+            const int part = c % cpr;
+            const int i = (c / cpr) % rows_out;
+            const int w = wb0 + c / (cpr * rows_out);
+            const int64_t dst = ((((int64_t)lr * W + w) * p.suffix_cap + i) * Hkv + g) * D + part * 8;
+            const uint16_t *ks, *vs;
+            if (i < p.hist_len) {
+                int src = p.parent ? p.parent[r * W + w] : w;
+                if (src < 0 || src >= W) { raise_error(p.err, kErrParent); src = w; }
+                const int64_t so = ((((int64_t)lr * W + src) * p.suffix_cap + i) * Hkv + g) * D + part * 8;
+                ks = p.suffix_k_in + so;
+                vs = p.suffix_v_in + so;
+            } else {
+                const int64_t so = (((int64_t)lr * W + w) * Hkv + g) * D + part * 8;
+                ks = p.k_new + so;
+                vs = p.v_new + so;
+            }
+            *(u32x4*)(p.suffix_k_out + dst) = *(const u32x4*)ks;
+            *(u32x4*)(p.suffix_v_out + dst) = *(const u32x4*)vs;
+        }
+    }
+    __syncthreads();
+
+    const int nkc = PP / 64;                      // 64-key prompt chunks
+    for (int blk = row0 + wave * 32; blk < row1; blk += 32 * (kDecThreads / kWave)) {
+        const int m = blk + n;                    // this lane's query row
+        const bool valid = m < row1;
+        const int w = valid ? m / G : 0;
+        const int hh = valid ? m % G : 0;
+        const int h = g * G + hh;
+        const int64_t qoff = (((int64_t)lr * W + w) * p.n_heads_q + h) * D;
+
+        u32x4 qreg[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            qreg[ks] = valid ? *(const u32x4*)(p.q + qoff + ks * 16 + hf * 8) : u32x4{0u, 0u, 0u, 0u};
+
+        f32x16 o[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+        float mrun = -INFINITY, lsum = 0.f;
+
+        for (int kc = 0; kc < nkc; ++kc) {
+            const int k0 = kc * 64;
+            f32x16 sacc[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const u32x4 a = *(const u32x4*)(k_lds + (k0 + kb * 32 + n) * KROW + ks * 16 + hf * 8);
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[ks]),
+                                                                       sacc[kb], 0, 0, 0);
+                }
+            }
+            const bool tail = k0 + 64 > P;
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float x = sacc[kb][i] * p.scale_log2;
+                    if (tail && k0 + kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3) >= P) x = -INFINITY;
+                    sacc[kb][i] = x;
+                    tmax = fmaxf(tmax, x);
+                }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const float mnew = fmaxf(mrun, tmax);  // finite: every chunk holds a prompt key
+            const float alpha = fast_exp2(mrun - mnew);
+            mrun = mnew;
+            float psum = 0.f;
+            uint32_t pk[2][8];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) {
+                    const float p0 = fast_exp2(sacc[kb][i] - mnew);
+                    const float p1 = fast_exp2(sacc[kb][i + 1] - mnew);
+                    psum += p0 + p1;
+                    pk[kb][i >> 1] = pack_bf16x2(p0, p1);
+                }
+            lsum = lsum * alpha + psum;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const u32x4 pb = {pk[kb][4 * j], pk[kb][4 * j + 1], pk[kb][4 * j + 2], pk[kb][4 * j + 3]};
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const u32x4 a = *(const u32x4*)(vt_lds + (db * 32 + n) * VROW + k0 + 16 * (2 * kb + j) + 8 * hf);
+                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pb), o[db], 0, 0, 0);
+                    }
+                }
+        }
+
+        // ---- the beam's own suffix: parent's history rows, then the new row ----
+        int src = w;
+        if (p.parent && p.hist_len > 0) {
+            src = p.parent[r * W + w];
+            if (src < 0 || src >= W) src = w;     // flagged by the suffix copy above
+        }
+        const int ns = p.hist_len + 1;
+        float sc[8];                              // host guarantees hist_len + 1 <= 8
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            sc[i] = -INFINITY;
+            if (i < ns) {
+                const uint16_t* kr = i < p.hist_len
+                    ? p.suffix_k_in + ((((int64_t)lr * W + src) * p.suffix_cap + i) * Hkv + g) * D
+                    : p.k_new + (((int64_t)lr * W + w) * Hkv + g) * D;
+                float part = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const u32x4 kv = *(const u32x4*)(kr + ks * 16 + hf * 8);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        part += bf16_bits_to_f32(qreg[ks][e] & 0xFFFFu) * bf16_bits_to_f32(kv[e] & 0xFFFFu);
+                        part += bf16_bits_to_f32(qreg[ks][e] >> 16) * bf16_bits_to_f32(kv[e] >> 16);
+                    }
+                }
+                part += __shfl_xor(part, 32);
+                sc[i] = part * p.scale_log2;
+            }
+        }
+        float smax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) smax = fmaxf(smax, sc[i]);
+        const float mnew = fmaxf(mrun, smax);     // finite: the new row is always there
+        const float alpha = fast_exp2(mrun - mnew);
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i < ns) {
+                const float pi = fast_exp2(sc[i] - mnew);
+                if (hf == 0) lsum += pi;          // both halves hold the same score
+                const uint16_t* vr = i < p.hist_len
+                    ? p.suffix_v_in + ((((int64_t)lr * W + src) * p.suffix_cap + i) * Hkv + g) * D
+                    : p.v_new + (((int64_t)lr * W + w) * Hkv + g) * D;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4) {
+                        const u32x2 vv = *(const u32x2*)(vr + db * 32 + 8 * i4 + 4 * hf);
+                        o[db][4 * i4 + 0] += pi * bf16_bits_to_f32(vv[0] & 0xFFFFu);
+                        o[db][4 * i4 + 1] += pi * bf16_bits_to_f32(vv[0] >> 16);
+                        o[db][4 * i4 + 2] += pi * bf16_bits_to_f32(vv[1] & 0xFFFFu);
+                        o[db][4 * i4 + 3] += pi * bf16_bits_to_f32(vv[1] >> 16);
+                    }
+            }
+        }
+
+        lsum += __shfl_xor(lsum, 32);
+        if (valid) {
+            const float inv = 1.f / lsum;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int d = db * 32 + 8 * i4 + 4 * hf;
+                    const float r0 = o[db][4 * i4] * inv, r1 = o[db][4 * i4 + 1] * inv;
+                    const float r2 = o[db][4 * i4 + 2] * inv, r3 = o[db][4 * i4 + 3] * inv;
+                    if constexpr (OUT_BF16) {
+                        *(u32x2*)((uint16_t*)p.out + qoff + d) = u32x2{pack_bf16x2(r0, r1), pack_bf16x2(r2, r3)};
+                    } else {
+                        *(f32x4*)((float*)p.out + qoff + d) = f32x4{r0, r1, r2, r3};
+                    }
+                }
+        }
+    }
+}
+
+template <int D, bool OUT_BF16>
+hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
+    const int n_units = p.n_layers * p.num_requests * p.n_heads_kv;
+    const int M = p.width * p.group;
+    const int blocks32 = (M + 31) / 32;
+    // enough workgroups to fill 256 CUs a few times over, whole 32-row blocks each
+    int chunks = (1024 + n_units - 1) / n_units;
+    chunks = max(1, min(chunks, blocks32));
+    const int chunk_rows = (blocks32 + chunks - 1) / chunks * 32;
+    chunks = (M + chunk_rows - 1) / chunk_rows;
+    const int64_t units_padded = ((int64_t)n_units + kNumXcd - 1) / kNumXcd * kNumXcd;
+    const int64_t blocks = units_padded * chunks;
+    if (blocks == 0) return hipSuccess;
+    const size_t lds = DecodeLds<D>::bytes(p.prompt_len);
+    auto kern = beam_decode_attn_kernel<D, OUT_BF16>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kDecThreads), lds, stream, p, chunks, chunk_rows);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t beam_decode_lds_bytes(int head_dim, int prompt_len) {
+    return head_dim == 128 ? DecodeLds<128>::bytes(prompt_len) : DecodeLds<64>::bytes(prompt_len);
+}
+
+hipError_t launch_beam_decode_attn(const DecodeParams& p, int head_dim, bool out_bf16,
+                                   hipStream_t stream) {
+    if (head_dim == 128)
+        return out_bf16 ? launch_variant<128, true>(p, stream) : launch_variant<128, false>(p, stream);
+    return out_bf16 ? launch_variant<64, true>(p, stream) : launch_variant<64, false>(p, stream);
+}
+
+}  // namespace slm

@@ -1,0 +1,93 @@
+// Internal launch interface between the C-ABI layer (slm_api.hip) and the
+// kernels.  Host-side validation happens before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace slm {
+
+// Device error codes written to the context's flag word.
+enum DeviceError : int {
+    kErrNone = 0,
+    kErrCuSeqlens = 1,     // cu_seqlens not monotone / out of [0,T] / length > max_seqlen
+    kErrParent = 2,        // parent index outside [0, W)
+};
+
+
+struct PrefillParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* cu;
+    void* out;
+    int* err;
+    int num_seqs, total_tokens, max_seqlen;
+    int n_heads_q, n_heads_kv, group;   // group = Hq / Hkv
+    int heads_per_block;                // query heads of one KV group per workgroup
+    int head_blocks;                    // group / heads_per_block
+    int q_tiles;                        // query tiles per sequence (from max_seqlen)
+    int n_units;                        // num_seqs * Hkv * head_blocks
+    float scale_log2;                   // softmax scale * log2(e)
+};
+hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, bool out_bf16,
+                               hipStream_t stream);
+
+struct GatherParams {
+    const void* hidden;
+    const int32_t* cu;
+    void* out;
+    int* err;
+    int num_seqs, total_tokens;
+    int64_t row_bytes;
+    bool vec16;                         // 16-byte copies (row and pointers aligned)
+};
+hipError_t launch_gather_last(const GatherParams& p, hipStream_t stream);
+
+struct ReorderParams {
+    const int32_t* parent;
+    const uint16_t* k_in;
+    const uint16_t* v_in;
+    uint16_t* k_out;
+    uint16_t* v_out;
+    int* err;
+    int n_layers, num_requests, width, rows, suffix_cap;
+    int row_elems;                      // Hkv * D
+};
+hipError_t launch_reorder_suffix(const ReorderParams& p, hipStream_t stream);
+
+struct DecodeParams {
+    const uint16_t* q;
+    const uint16_t* prefix_k;
+    const uint16_t* prefix_v;
+    const uint16_t* suffix_k_in;
+    const uint16_t* suffix_v_in;
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    const int32_t* parent;
+    uint16_t* suffix_k_out;
+    uint16_t* suffix_v_out;
+    void* out;
+    int* err;
+    int n_layers, num_requests, width, prompt_len, hist_len, suffix_cap;
+    int n_heads_q, n_heads_kv, group;
+    float scale_log2;
+};
+hipError_t launch_beam_decode_attn(const DecodeParams& p, int head_dim, bool out_bf16,
+                                   hipStream_t stream);
+
+struct TopkParams {
+    const float* logprobs;
+    const float* cum;
+    int32_t* tokens;
+    int32_t* parent;
+    float* cum_out;
+    uint64_t* stage1;                   // workspace: [R, Win, even(W)] keys, 0 = empty
+    int num_requests, beams_in, vocab, width;
+};
+hipError_t launch_beam_topk_merge(const TopkParams& p, hipStream_t stream);
+size_t beam_topk_workspace_bytes(int max_requests, int max_beams);
+size_t beam_decode_lds_bytes(int head_dim, int prompt_len);
+constexpr int kTopkMaxWidth = 512;
+constexpr int kDecodeMaxSuffix = 8;     // hist_len + 1 <= 8
+
+}  // namespace slm

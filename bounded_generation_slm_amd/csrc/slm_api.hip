@@ -1,0 +1,372 @@
+// C-ABI layer of libslm: context, load-time workspace, host-side validation
+// and dispatch to the kernels.  The operations and their conventions are
+// declared in include/slm.h.
+//
+// The context is the load-time plan of the page "SLM 生成式高并发推理引擎：
+// 延迟约束下的有效吞吐优化" (§1.2 and §02): request count, beam width and
+// vocabulary are bounded before serving, so the only workspace (the top-k
+// stage-1 keys and a device error flag) is allocated once at create time and
+// no call allocates or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "../../include/slm.h"
+#include "kernels.h"
+
+struct slm_ctx {
+    int device = 0;
+    bool dry_run = false;   // device < 0: validate arguments only, touch no device
+    hipStream_t stream = nullptr;
+    slm_caps caps{};
+    uint64_t* topk_ws = nullptr;
+    size_t topk_ws_bytes = 0;
+    int* err_flag = nullptr;
+    size_t max_lds = 0;
+    char last_error[512] = {0};
+};
+
+namespace {
+
+slm_status fail(slm_ctx* ctx, slm_status s, const char* fmt, ...) {
+    if (ctx) {
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(ctx->last_error, sizeof ctx->last_error, fmt, ap);
+        va_end(ap);
+    }
+    return s;
+}
+
+slm_status ok(slm_ctx* ctx) {
+    ctx->last_error[0] = 0;
+    return SLM_OK;
+}
+
+// Validation passed: a dry-run context stops here, others launch.
+#define SLM_LAUNCH(ctx, call, what) \
+    ((ctx)->dry_run ? ok(ctx) : launched((ctx), (call), (what)))
+
+slm_status launched(slm_ctx* ctx, hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(ctx, SLM_ERR_DEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok(ctx);
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Sets the context's device current for the launches that follow.
+slm_status enter(slm_ctx* ctx) {
+    if (!ctx) return SLM_ERR_INVALID_ARG;
+    if (ctx->dry_run) return SLM_OK;
+    if (hipSetDevice(ctx->device) != hipSuccess)
+        return fail(ctx, SLM_ERR_DEVICE, "hipSetDevice(%d) failed", ctx->device);
+    return SLM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int slm_abi_version(void) { return SLM_ABI_VERSION; }
+
+const char* slm_status_string(slm_status s) {
+    switch (s) {
+        case SLM_OK: return "SLM_OK";
+        case SLM_ERR_INVALID_ARG: return "SLM_ERR_INVALID_ARG";
+        case SLM_ERR_UNSUPPORTED: return "SLM_ERR_UNSUPPORTED";
+        case SLM_ERR_CAPACITY: return "SLM_ERR_CAPACITY";
+        case SLM_ERR_ALIAS: return "SLM_ERR_ALIAS";
+        case SLM_ERR_DEVICE: return "SLM_ERR_DEVICE";
+        case SLM_ERR_OOM: return "SLM_ERR_OOM";
+    }
+    return "SLM_ERR_UNKNOWN";
+}
+
+const char* slm_ctx_last_error(const slm_ctx* ctx) { return ctx ? ctx->last_error : "null context"; }
+
+slm_status slm_ctx_create(int device, const slm_caps* caps, slm_ctx** out) {
+    if (!out) return SLM_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (device < 0) {                       // dry run: host-side validation only
+        slm_ctx* ctx = new (std::nothrow) slm_ctx;
+        if (!ctx) return SLM_ERR_OOM;
+        ctx->dry_run = true;
+        ctx->device = -1;
+        slm_caps c = caps ? *caps : slm_caps{};
+        if (c.max_requests <= 0) c.max_requests = 64;
+        if (c.max_beams <= 0) c.max_beams = slm::kTopkMaxWidth;
+        if (c.max_vocab <= 0) c.max_vocab = 262144;
+        ctx->caps = c;
+        ctx->max_lds = 160 * 1024;          // gfx950 LDS per workgroup
+        *out = ctx;
+        return SLM_OK;
+    }
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) return SLM_ERR_DEVICE;
+    slm_ctx* ctx = new (std::nothrow) slm_ctx;
+    if (!ctx) return SLM_ERR_OOM;
+    ctx->device = device;
+    slm_caps c = caps ? *caps : slm_caps{};
+    if (c.max_requests <= 0) c.max_requests = 64;
+    if (c.max_beams <= 0) c.max_beams = slm::kTopkMaxWidth;
+    if (c.max_vocab <= 0) c.max_vocab = 262144;
+    ctx->caps = c;
+    if (hipSetDevice(device) != hipSuccess) {
+        delete ctx;
+        return SLM_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) {
+        delete ctx;
+        return SLM_ERR_DEVICE;
+    }
+    ctx->max_lds = prop.sharedMemPerBlock;
+    ctx->topk_ws_bytes = slm::beam_topk_workspace_bytes(c.max_requests, c.max_beams);
+    if (hipMalloc((void**)&ctx->topk_ws, ctx->topk_ws_bytes) != hipSuccess ||
+        hipMalloc((void**)&ctx->err_flag, sizeof(int)) != hipSuccess ||
+        hipMemset(ctx->err_flag, 0, sizeof(int)) != hipSuccess) {
+        if (ctx->topk_ws) (void)hipFree(ctx->topk_ws);
+        if (ctx->err_flag) (void)hipFree(ctx->err_flag);
+        delete ctx;
+        return SLM_ERR_OOM;
+    }
+    *out = ctx;
+    return SLM_OK;
+}
+
+void slm_ctx_destroy(slm_ctx* ctx) {
+    if (!ctx) return;
+    if (!ctx->dry_run && hipSetDevice(ctx->device) == hipSuccess) {
+        (void)hipDeviceSynchronize();
+        (void)hipFree(ctx->topk_ws);
+        (void)hipFree(ctx->err_flag);
+    }
+    delete ctx;
+}
+
+slm_status slm_ctx_set_stream(slm_ctx* ctx, void* hip_stream) {
+    if (!ctx) return SLM_ERR_INVALID_ARG;
+    ctx->stream = (hipStream_t)hip_stream;
+    return ok(ctx);
+}
+
+slm_status slm_ctx_check(slm_ctx* ctx) {
+    slm_status s = enter(ctx);
+    if (s != SLM_OK) return s;
+    if (ctx->dry_run) return ok(ctx);
+    if (hipStreamSynchronize(ctx->stream) != hipSuccess)
+        return fail(ctx, SLM_ERR_DEVICE, "stream synchronisation failed: %s", hipGetErrorString(hipGetLastError()));
+    int flag = 0;
+    if (hipMemcpy(&flag, ctx->err_flag, sizeof flag, hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(ctx, SLM_ERR_DEVICE, "reading the device error flag failed");
+    if (flag != 0) {
+        (void)hipMemset(ctx->err_flag, 0, sizeof(int));
+        if (flag == slm::kErrCuSeqlens)
+            return fail(ctx, SLM_ERR_INVALID_ARG, "cu_seqlens: not non-decreasing in [0,T] or a length above max_seqlen");
+        return fail(ctx, SLM_ERR_INVALID_ARG, "parent index outside [0, width)");
+    }
+    return ok(ctx);
+}
+
+slm_status slm_packed_prefill_attn(slm_ctx* ctx, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                                   int32_t max_seqlen, int32_t n_heads_q, int32_t n_heads_kv,
+                                   int32_t head_dim, float scale, void* out, slm_dtype out_dtype) {
+    slm_status s = enter(ctx);
+    if (s != SLM_OK) return s;
+    if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0 || n_heads_q <= 0 || n_heads_kv <= 0 || head_dim <= 0)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: negative size or non-positive head count / head_dim");
+    if (n_heads_q % n_heads_kv != 0)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: n_heads_q %% n_heads_kv != 0");
+    if (head_dim != 64 && head_dim != 128)
+        return fail(ctx, SLM_ERR_UNSUPPORTED, "prefill: head_dim %d (supported: 64, 128)", head_dim);
+    if (out_dtype != SLM_F32 && out_dtype != SLM_BF16)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: unknown out_dtype");
+    if (!(scale > 0.f) || !std::isfinite(scale))
+        return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: scale must be finite and positive");
+    if (!cu_seqlens) return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: cu_seqlens is NULL");
+    if (total_tokens == 0 || num_seqs == 0 || max_seqlen == 0) return ok(ctx);
+    if (!q || !k || !v || !out) return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: NULL tensor");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: tensors must be 16-byte aligned");
+    if (max_seqlen > total_tokens)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: max_seqlen %d > total_tokens %d", max_seqlen, total_tokens);
+    const size_t T = (size_t)total_tokens, D = (size_t)head_dim;
+    const size_t qb = T * n_heads_q * D * 2, kb = T * n_heads_kv * D * 2;
+    const size_t ob = T * n_heads_q * D * (out_dtype == SLM_F32 ? 4 : 2);
+    const size_t cb = ((size_t)num_seqs + 1) * 4;
+    if (overlaps(out, ob, q, qb) || overlaps(out, ob, k, kb) || overlaps(out, ob, v, kb) ||
+        overlaps(out, ob, cu_seqlens, cb))
+        return fail(ctx, SLM_ERR_ALIAS, "prefill: out overlaps an input");
+    slm::PrefillParams p{};
+    p.q = q; p.k = k; p.v = v; p.cu = cu_seqlens; p.out = out; p.err = ctx->err_flag;
+    p.num_seqs = num_seqs; p.total_tokens = total_tokens; p.max_seqlen = max_seqlen;
+    p.n_heads_q = n_heads_q; p.n_heads_kv = n_heads_kv; p.group = n_heads_q / n_heads_kv;
+    p.heads_per_block = (p.group % 2 == 0) ? 2 : 1;
+    p.head_blocks = p.group / p.heads_per_block;
+    const int qt_rows = 128 / p.heads_per_block;
+    p.q_tiles = (max_seqlen + qt_rows - 1) / qt_rows;
+    const int64_t units = (int64_t)num_seqs * n_heads_kv * p.head_blocks;
+    if (units > INT32_MAX / 8) return fail(ctx, SLM_ERR_UNSUPPORTED, "prefill: too many sequences x heads");
+    p.n_units = (int)units;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    return SLM_LAUNCH(ctx, slm::launch_prefill_attn(p, head_dim, out_dtype == SLM_BF16, ctx->stream), "prefill");
+}
+
+slm_status slm_gather_last(slm_ctx* ctx, const void* hidden, const int32_t* cu_seqlens, int32_t num_seqs,
+                           int32_t total_tokens, int32_t hidden_dim, slm_dtype dtype, void* out) {
+    slm_status s = enter(ctx);
+    if (s != SLM_OK) return s;
+    if (num_seqs < 0 || total_tokens < 0 || hidden_dim <= 0)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "gather: negative size or hidden_dim <= 0");
+    if (dtype != SLM_F32 && dtype != SLM_BF16) return fail(ctx, SLM_ERR_INVALID_ARG, "gather: unknown dtype");
+    if (num_seqs == 0) return ok(ctx);
+    if (!cu_seqlens || !out || (!hidden && total_tokens > 0))
+        return fail(ctx, SLM_ERR_INVALID_ARG, "gather: NULL pointer");
+    const size_t row = (size_t)hidden_dim * (dtype == SLM_F32 ? 4 : 2);
+    if (overlaps(out, row * num_seqs, hidden, row * total_tokens) ||
+        overlaps(out, row * num_seqs, cu_seqlens, ((size_t)num_seqs + 1) * 4))
+        return fail(ctx, SLM_ERR_ALIAS, "gather: out overlaps an input");
+    slm::GatherParams p{};
+    p.hidden = hidden; p.cu = cu_seqlens; p.out = out; p.err = ctx->err_flag;
+    p.num_seqs = num_seqs; p.total_tokens = total_tokens; p.row_bytes = (int64_t)row;
+    p.vec16 = (row % 16 == 0) && aligned16(hidden) && aligned16(out);
+    if (((uintptr_t)hidden & 1) || ((uintptr_t)out & 1))
+        return fail(ctx, SLM_ERR_INVALID_ARG, "gather: tensors must be 2-byte aligned");
+    return SLM_LAUNCH(ctx, slm::launch_gather_last(p, ctx->stream), "gather");
+}
+
+slm_status slm_beam_decode_attn(slm_ctx* ctx, const slm_beam_attn_args* a) {
+    slm_status s = enter(ctx);
+    if (s != SLM_OK) return s;
+    if (!a) return fail(ctx, SLM_ERR_INVALID_ARG, "decode: NULL args");
+    if (a->n_layers <= 0 || a->num_requests <= 0 || a->width <= 0 || a->prompt_len < 0 || a->hist_len < 0 ||
+        a->suffix_cap <= 0 || a->n_heads_q <= 0 || a->n_heads_kv <= 0 || a->head_dim <= 0)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "decode: a size is out of range");
+    if (a->n_heads_q % a->n_heads_kv != 0) return fail(ctx, SLM_ERR_INVALID_ARG, "decode: n_heads_q %% n_heads_kv != 0");
+    if (a->hist_len + 1 > a->suffix_cap)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "decode: hist_len + 1 > suffix_cap");
+    if (a->hist_len + 1 > slm::kDecodeMaxSuffix)
+        return fail(ctx, SLM_ERR_UNSUPPORTED, "decode: more than %d suffix rows", slm::kDecodeMaxSuffix);
+    if (a->head_dim != 64 && a->head_dim != 128)
+        return fail(ctx, SLM_ERR_UNSUPPORTED, "decode: head_dim %d (supported: 64, 128)", a->head_dim);
+    if (a->out_dtype != SLM_F32 && a->out_dtype != SLM_BF16) return fail(ctx, SLM_ERR_INVALID_ARG, "decode: unknown out_dtype");
+    if (!(a->scale > 0.f) || !std::isfinite(a->scale)) return fail(ctx, SLM_ERR_INVALID_ARG, "decode: bad scale");
+    if (!a->q || !a->k_new || !a->v_new || !a->out || !a->suffix_k_out || !a->suffix_v_out ||
+        (a->prompt_len > 0 && (!a->prefix_k || !a->prefix_v)) ||
+        (a->hist_len > 0 && (!a->suffix_k_in || !a->suffix_v_in)))
+        return fail(ctx, SLM_ERR_INVALID_ARG, "decode: NULL tensor");
+    const void* ptrs[] = {a->q, a->prefix_k, a->prefix_v, a->suffix_k_in, a->suffix_v_in, a->k_new, a->v_new,
+                          a->suffix_k_out, a->suffix_v_out, a->out};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return fail(ctx, SLM_ERR_INVALID_ARG, "decode: tensors must be 16-byte aligned");
+    const size_t lds = slm::beam_decode_lds_bytes(a->head_dim, a->prompt_len);
+    if (lds > ctx->max_lds)
+        return fail(ctx, SLM_ERR_UNSUPPORTED, "decode: prompt_len %d x head_dim %d needs %zu B of LDS (> %zu)",
+                    a->prompt_len, a->head_dim, lds, ctx->max_lds);
+    const size_t NL = a->n_layers, R = a->num_requests, W = a->width, D = a->head_dim;
+    const size_t Hq = a->n_heads_q, Hkv = a->n_heads_kv;
+    if ((NL * R * W * Hq) > (size_t)INT32_MAX || NL * R * Hkv * 8 > (size_t)INT32_MAX)
+        return fail(ctx, SLM_ERR_UNSUPPORTED, "decode: too many rows");
+    const size_t qb = NL * R * W * Hq * D * 2, ob = NL * R * W * Hq * D * (a->out_dtype == SLM_F32 ? 4 : 2);
+    const size_t pb = NL * R * a->prompt_len * Hkv * D * 2, sb = NL * R * W * a->suffix_cap * Hkv * D * 2;
+    const size_t nb = NL * R * W * Hkv * D * 2, parb = R * W * 4;
+    struct Buf { const void* p; size_t n; };
+    const Buf ins[] = {{a->q, qb}, {a->prefix_k, pb}, {a->prefix_v, pb}, {a->suffix_k_in, sb}, {a->suffix_v_in, sb},
+                       {a->k_new, nb}, {a->v_new, nb}, {a->parent, parb}};
+    const Buf outs[] = {{a->out, ob}, {a->suffix_k_out, sb}, {a->suffix_v_out, sb}};
+    for (const Buf& o : outs)
+        for (const Buf& i : ins)
+            if (overlaps(o.p, o.n, i.p, i.n)) return fail(ctx, SLM_ERR_ALIAS, "decode: an output overlaps an input");
+    if (overlaps(outs[0].p, outs[0].n, outs[1].p, outs[1].n) || overlaps(outs[0].p, outs[0].n, outs[2].p, outs[2].n) ||
+        overlaps(outs[1].p, outs[1].n, outs[2].p, outs[2].n))
+        return fail(ctx, SLM_ERR_ALIAS, "decode: outputs overlap each other");
+    slm::DecodeParams p{};
+    p.q = a->q; p.prefix_k = a->prefix_k; p.prefix_v = a->prefix_v;
+    p.suffix_k_in = a->suffix_k_in; p.suffix_v_in = a->suffix_v_in; p.k_new = a->k_new; p.v_new = a->v_new;
+    p.parent = a->parent; p.suffix_k_out = a->suffix_k_out; p.suffix_v_out = a->suffix_v_out; p.out = a->out;
+    p.err = ctx->err_flag;
+    p.n_layers = a->n_layers; p.num_requests = a->num_requests; p.width = a->width; p.prompt_len = a->prompt_len;
+    p.hist_len = a->hist_len; p.suffix_cap = a->suffix_cap; p.n_heads_q = a->n_heads_q;
+    p.n_heads_kv = a->n_heads_kv; p.group = a->n_heads_q / a->n_heads_kv;
+    p.scale_log2 = a->scale * 1.4426950408889634f;
+    return SLM_LAUNCH(ctx, slm::launch_beam_decode_attn(p, a->head_dim, a->out_dtype == SLM_BF16, ctx->stream),
+                      "decode");
+}
+
+slm_status slm_beam_topk_merge(slm_ctx* ctx, const float* logprobs, const float* cum, int32_t num_requests,
+                               int32_t beams_in, int32_t vocab, int32_t width, int32_t* tokens, int32_t* parent,
+                               float* cum_out) {
+    slm_status s = enter(ctx);
+    if (s != SLM_OK) return s;
+    if (num_requests < 0 || beams_in <= 0 || vocab <= 0 || width <= 0)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "topk: a size is out of range");
+    if ((int64_t)width > (int64_t)beams_in * vocab)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "topk: width %d > beams_in * vocab", width);
+    if ((int64_t)beams_in * vocab >= ((int64_t)1 << 31))
+        return fail(ctx, SLM_ERR_UNSUPPORTED, "topk: beams_in * vocab must be below 2^31");
+    if (width > slm::kTopkMaxWidth) return fail(ctx, SLM_ERR_UNSUPPORTED, "topk: width %d > %d", width, slm::kTopkMaxWidth);
+    if (num_requests > ctx->caps.max_requests || beams_in > ctx->caps.max_beams || width > ctx->caps.max_beams ||
+        vocab > ctx->caps.max_vocab)
+        return fail(ctx, SLM_ERR_CAPACITY, "topk: beyond the context caps (requests %d, beams %d, vocab %d)",
+                    ctx->caps.max_requests, ctx->caps.max_beams, ctx->caps.max_vocab);
+    if (num_requests == 0) return ok(ctx);
+    if (!logprobs || !cum || !tokens || !parent || !cum_out) return fail(ctx, SLM_ERR_INVALID_ARG, "topk: NULL tensor");
+    if (((uintptr_t)logprobs & 3) || ((uintptr_t)cum & 3) || ((uintptr_t)tokens & 3) || ((uintptr_t)parent & 3) ||
+        ((uintptr_t)cum_out & 3))
+        return fail(ctx, SLM_ERR_INVALID_ARG, "topk: tensors must be 4-byte aligned");
+    const size_t R = num_requests;
+    const size_t lpb = R * beams_in * (size_t)vocab * 4, cb = R * beams_in * 4, ob = R * width * 4;
+    const void* outs[] = {tokens, parent, cum_out};
+    for (const void* o : outs)
+        if (overlaps(o, ob, logprobs, lpb) || overlaps(o, ob, cum, cb))
+            return fail(ctx, SLM_ERR_ALIAS, "topk: an output overlaps an input");
+    if (overlaps(tokens, ob, parent, ob) || overlaps(tokens, ob, cum_out, ob) || overlaps(parent, ob, cum_out, ob))
+        return fail(ctx, SLM_ERR_ALIAS, "topk: outputs overlap each other");
+    slm::TopkParams p{};
+    p.logprobs = logprobs; p.cum = cum; p.tokens = tokens; p.parent = parent; p.cum_out = cum_out;
+    p.stage1 = ctx->topk_ws; p.num_requests = num_requests; p.beams_in = beams_in; p.vocab = vocab; p.width = width;
+    return SLM_LAUNCH(ctx, slm::launch_beam_topk_merge(p, ctx->stream), "topk");
+}
+
+slm_status slm_beam_reorder_suffix(slm_ctx* ctx, int32_t n_layers, int32_t num_requests, int32_t width,
+                                   int32_t rows, int32_t suffix_cap, int32_t n_heads_kv, int32_t head_dim,
+                                   const int32_t* parent, const uint16_t* k_in, const uint16_t* v_in,
+                                   uint16_t* k_out, uint16_t* v_out) {
+    slm_status s = enter(ctx);
+    if (s != SLM_OK) return s;
+    if (n_layers <= 0 || num_requests <= 0 || width <= 0 || rows < 0 || suffix_cap <= 0 || rows > suffix_cap ||
+        n_heads_kv <= 0 || head_dim <= 0)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "reorder: a size is out of range");
+    if ((n_heads_kv * head_dim) % 8 != 0)
+        return fail(ctx, SLM_ERR_UNSUPPORTED, "reorder: n_heads_kv * head_dim must be a multiple of 8");
+    if (rows == 0) return ok(ctx);
+    if (!parent || !k_in || !v_in || !k_out || !v_out) return fail(ctx, SLM_ERR_INVALID_ARG, "reorder: NULL tensor");
+    if (!aligned16(k_in) || !aligned16(v_in) || !aligned16(k_out) || !aligned16(v_out))
+        return fail(ctx, SLM_ERR_INVALID_ARG, "reorder: tensors must be 16-byte aligned");
+    const size_t sb = (size_t)n_layers * num_requests * width * suffix_cap * n_heads_kv * head_dim * 2;
+    const size_t pb = (size_t)num_requests * width * 4;
+    const void* outs[] = {k_out, v_out};
+    for (const void* o : outs)
+        if (overlaps(o, sb, k_in, sb) || overlaps(o, sb, v_in, sb) || overlaps(o, sb, parent, pb))
+            return fail(ctx, SLM_ERR_ALIAS, "reorder: an output overlaps an input");
+    if (overlaps(k_out, sb, v_out, sb)) return fail(ctx, SLM_ERR_ALIAS, "reorder: outputs overlap each other");
+    slm::ReorderParams p{};
+    p.parent = parent; p.k_in = k_in; p.v_in = v_in; p.k_out = k_out; p.v_out = v_out; p.err = ctx->err_flag;
+    p.n_layers = n_layers; p.num_requests = num_requests; p.width = width; p.rows = rows; p.suffix_cap = suffix_cap;
+    p.row_elems = n_heads_kv * head_dim;
+    return SLM_LAUNCH(ctx, slm::launch_reorder_suffix(p, ctx->stream), "reorder");
+}
+
+}  // extern "C"

@@ -1,0 +1,191 @@
+/*
+ * slm.h -- C ABI of libslm, the attention hot path of a bounded-generation
+ * small-language-model engine, hand-written in HIP for AMD MI355X (gfx950).
+ *
+ * Source of the operations: the page "SLM 生成式高并发推理引擎：延迟约束下的
+ * 有效吞吐优化" (abstract, §1.1 "两类在线执行形式", §1.2 "输入与状态边界").
+ *   - Prefill-only requests run one prefill over a batch of variable-length
+ *     samples, computing only the valid tokens of each sample (§1.2), and take
+ *     their result at each sequence's last valid token (§1.1).
+ *   - Beam-search requests run a prefill and then a fixed number of decode
+ *     steps at a fixed width; every step merges per-beam candidates with the
+ *     cumulative scores and keeps a fixed number, with parent indices (§1.1).
+ *     All beams of one request share one prompt K/V and keep their own short
+ *     suffix K/V (§1.2), and all state is planned at load time (§1.2, §02).
+ *
+ * Conventions for every call below:
+ *   - Tensor arguments are DEVICE pointers, owned by the caller, contiguous,
+ *     row-major in the layout stated, and 16-byte aligned.  bf16 tensors are
+ *     passed as their 16-bit storage (uint16_t).
+ *   - Calls are asynchronous and ordered on the context's stream.  The
+ *     library never allocates or synchronises inside a call; the context owns
+ *     one workspace allocated by slm_ctx_create and sized by slm_caps.
+ *   - The return value reports host-side validation and launch failures.  No
+ *     C++ exception crosses the ABI.  On an error nothing is launched, and
+ *     slm_ctx_last_error() gives a human-readable detail.
+ *   - Contents of device arguments (cu_seqlens, parent) cannot be validated
+ *     on the host; kernels bound-check them and, on a violation, set the
+ *     context's device error flag, which slm_ctx_check() reads
+ *     (SLM_ERR_INVALID_ARG).  The affected outputs are then unspecified, but
+ *     no kernel reads or writes out of bounds whatever those contents are.
+ *   - A context is not thread-safe; calls that overlap on one stream are
+ *     ordered, calls from several host threads on one context race.
+ */
+#ifndef SLM_H
+#define SLM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SLM_ABI_VERSION 1
+
+typedef enum {
+    SLM_OK = 0,
+    SLM_ERR_INVALID_ARG = 1,   /* a size, pointer or device-side index is wrong   */
+    SLM_ERR_UNSUPPORTED = 2,   /* a legal shape this build has no kernel for      */
+    SLM_ERR_CAPACITY = 3,      /* beyond the caps the context was created with    */
+    SLM_ERR_ALIAS = 4,         /* an output overlaps an input                     */
+    SLM_ERR_DEVICE = 5,        /* a HIP runtime call or launch failed             */
+    SLM_ERR_OOM = 6            /* the workspace could not be allocated            */
+} slm_status;
+
+typedef enum { SLM_BF16 = 0, SLM_F32 = 1 } slm_dtype;
+
+typedef struct slm_ctx slm_ctx;   /* opaque: device, stream, workspace, last error */
+
+/* Load-time capacity plan (§1.2: input length, beam width and step count are
+ * bounded before deployment, so state is preallocated).  Fields <= 0 are
+ * replaced by the defaults in parentheses. */
+typedef struct {
+    int32_t max_requests;   /* requests per beam call                 (64)      */
+    int32_t max_beams;      /* beam width and beams in                (512)     */
+    int32_t max_vocab;      /* vocabulary size                        (262144)  */
+} slm_caps;
+
+/* Create a context on HIP device `device`: sets that device current,
+ * allocates the top-k workspace (about max_requests * max_beams^2 * 8 bytes)
+ * and uses the null stream until slm_ctx_set_stream.  *out is NULL on error.
+ * device < 0 creates a dry-run context: every call performs its host-side
+ * validation and returns its status without touching any device (usable on
+ * machines without a GPU, e.g. to check argument handling). */
+slm_status slm_ctx_create(int device, const slm_caps *caps, slm_ctx **out);
+void slm_ctx_destroy(slm_ctx *ctx);
+/* Order later calls on `hip_stream` (a hipStream_t; NULL = null stream). */
+slm_status slm_ctx_set_stream(slm_ctx *ctx, void *hip_stream);
+/* Synchronise the stream and read (then clear) the device error flag. */
+slm_status slm_ctx_check(slm_ctx *ctx);
+const char *slm_status_string(slm_status s);
+const char *slm_ctx_last_error(const slm_ctx *ctx);
+int slm_abi_version(void);
+
+/*
+ * Packed causal GQA prefill attention (abstract: Packed Prefill; §1.2: keep
+ * each sequence's valid length, compute valid tokens only).
+ *   q           [T, Hq, D]  bf16    queries, T = total_tokens packed tokens
+ *   k, v        [T, Hkv, D] bf16    keys / values, after any position encoding
+ *   cu_seqlens  [B+1] int32 DEVICE  sequence b is tokens cu[b] .. cu[b+1]-1;
+ *               the caller guarantees cu[0] = 0, non-decreasing, cu[B] = T,
+ *               every length <= max_seqlen (violations: device error flag)
+ *   out         [T, Hq, D]  fp32 or bf16 (out_dtype)
+ * For token i of sequence b and query head h:
+ *   out = softmax_j(scale * q_i . k_j) v_j  over keys j = cu[b] .. i
+ * (causal, diagonal included, no attention across sequences); query head h
+ * reads KV head h / (Hq/Hkv).  Supported: head_dim 64 or 128, Hq % Hkv == 0.
+ * Empty sequences are allowed and produce no rows.  out must not overlap
+ * q, k, v or cu_seqlens.
+ */
+slm_status slm_packed_prefill_attn(slm_ctx *ctx, const uint16_t *q, const uint16_t *k,
+                                   const uint16_t *v, const int32_t *cu_seqlens,
+                                   int32_t num_seqs, int32_t total_tokens,
+                                   int32_t max_seqlen, int32_t n_heads_q,
+                                   int32_t n_heads_kv, int32_t head_dim, float scale,
+                                   void *out, slm_dtype out_dtype);
+
+/*
+ * Last-valid-token gather (§1.1: prefill-only outputs come from each
+ * sequence's last valid token position).
+ *   hidden [T, H] (dtype: 2 or 4 bytes per element), cu_seqlens as above,
+ *   out [B, H]: out[b] = hidden[cu[b+1]-1], bit copy; an empty sequence
+ *   gives a zero row.  out must not overlap hidden.
+ */
+slm_status slm_gather_last(slm_ctx *ctx, const void *hidden, const int32_t *cu_seqlens,
+                           int32_t num_seqs, int32_t total_tokens, int32_t hidden_dim,
+                           slm_dtype dtype, void *out);
+
+/*
+ * Beam decode attention over a shared prompt K/V and per-beam suffix K/V
+ * (§1.2: beams of one request share one prompt K/V and keep short suffixes;
+ * §1.1: parent indices carry beams across steps).  One call covers all
+ * n_layers layers of one decode step.  Shapes (NL layers, R requests, W beams,
+ * P prompt rows, S_cap suffix capacity):
+ *   q            [NL, R, W, Hq, D]        bf16
+ *   prefix_k/v   [NL, R, P, Hkv, D]       bf16  shared by the W beams
+ *   suffix_k_in/v_in [NL, R, W, S_cap, Hkv, D] bf16  rows 0..hist_len-1, in
+ *                the beam order BEFORE the last merge (may be NULL if hist_len = 0)
+ *   k_new/v_new  [NL, R, W, Hkv, D]       bf16  this step's key/value row
+ *   parent       [R, W] int32 DEVICE      last merge's parents, or NULL = identity
+ *   suffix_k_out/v_out [NL, R, W, S_cap, Hkv, D]  rows 0..hist_len written:
+ *                rows < hist_len = suffix_in[parent[j]] (bit copy), row
+ *                hist_len = k_new/v_new; other rows untouched
+ *   out          [NL, R, W, Hq, D]        fp32 or bf16
+ * For beam j and query head h (KV head h / (Hq/Hkv)) the keys are the P
+ * prompt rows, the hist_len history rows of beam parent[j] and the new row,
+ * all visible.  Needs hist_len + 1 <= S_cap, hist_len + 1 <= 8, head_dim 64
+ * or 128, and the prompt K and V^T of one (layer, request, KV head) must fit
+ * in one workgroup's LDS (P <= 576 at D = 64, P <= 256 at D = 128), else
+ * SLM_ERR_UNSUPPORTED.  Outputs must not overlap any input or each other.
+ * parent values outside [0, W) set the device error flag.
+ */
+typedef struct {
+    int32_t n_layers, num_requests, width, prompt_len, hist_len, suffix_cap;
+    int32_t n_heads_q, n_heads_kv, head_dim;
+    float scale;
+    const uint16_t *q, *prefix_k, *prefix_v, *suffix_k_in, *suffix_v_in, *k_new, *v_new;
+    const int32_t *parent;
+    uint16_t *suffix_k_out, *suffix_v_out;
+    void *out;
+    slm_dtype out_dtype;
+} slm_beam_attn_args;
+slm_status slm_beam_decode_attn(slm_ctx *ctx, const slm_beam_attn_args *args);
+
+/*
+ * Beam top-k merge (§1.1: each step takes local candidates from every beam's
+ * token distribution, merges them with the cumulative scores and keeps a
+ * fixed number; the first step starts from the prefill's log-probs).
+ *   logprobs [R, Win, V] fp32, cum [R, Win] fp32 (device)
+ *   tokens, parent [R, W] int32; cum_out [R, W] fp32
+ * For request r the candidates are (b, v) with score = cum[r,b] +
+ * logprobs[r,b,v], one IEEE fp32 addition; they are ranked by score
+ * descending, then by flat index f = b*V + v ascending (this total order makes
+ * the result unique), and the first W are written in that order: token =
+ * f mod V, parent = f div V, cum_out = score.  The first step passes Win = 1.
+ * Needs 1 <= W <= Win*V, W <= 512, Win*V < 2^31, R <= caps.max_requests,
+ * Win, W <= caps.max_beams, V <= caps.max_vocab.  NaN scores are a caller
+ * error (their rank is unspecified).  Outputs must not overlap the inputs.
+ */
+slm_status slm_beam_topk_merge(slm_ctx *ctx, const float *logprobs, const float *cum,
+                               int32_t num_requests, int32_t beams_in, int32_t vocab,
+                               int32_t width, int32_t *tokens, int32_t *parent,
+                               float *cum_out);
+
+/*
+ * Suffix K/V reorder after a merge (§1.1 parent index, §1.2 per-beam suffix):
+ *   k_out[l,r,j,i] = k_in[l,r,parent[r,j],i] for rows i < rows, same for V;
+ *   [NL, R, W, S_cap, Hkv, D] bf16 storage.  Rows >= rows are untouched.
+ *   Needs n_heads_kv * head_dim % 8 == 0.  Outputs must not overlap inputs
+ *   (no in-place gather).  parent values outside [0, W) set the device
+ *   error flag; those rows are not written.
+ */
+slm_status slm_beam_reorder_suffix(slm_ctx *ctx, int32_t n_layers, int32_t num_requests,
+                                   int32_t width, int32_t rows, int32_t suffix_cap,
+                                   int32_t n_heads_kv, int32_t head_dim,
+                                   const int32_t *parent, const uint16_t *k_in,
+                                   const uint16_t *v_in, uint16_t *k_out, uint16_t *v_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SLM_H */

@@ -1,0 +1,126 @@
+"""The C-ABI library on CPU: it loads, exports every function include/slm.h
+declares, and its host-side validation (run through a dry-run context,
+device -1, which launches nothing) returns the documented statuses."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import bounded_generation_slm_amd as slm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "slm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(slm_[a-z_]+)\s*\(", text))
+
+
+def test_exports_every_declared_symbol():
+    declared = _declared()
+    assert "slm_packed_prefill_attn" in declared and "slm_beam_topk_merge" in declared
+    lib = ctypes.CDLL(slm.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert declared == set(slm.EXPORTED)
+    assert slm.abi_version() == 1
+
+
+@pytest.fixture
+def dry():
+    return slm.Context(device=-1)
+
+
+def _bf(*shape):
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def _status(fn):
+    try:
+        fn()
+    except slm.SlmError as e:
+        return e.status
+    return slm.SLM_OK
+
+
+def test_prefill_validation(dry):
+    q, k, v = _bf(10, 4, 64), _bf(10, 2, 64), _bf(10, 2, 64)
+    cu = torch.tensor([0, 3, 10], dtype=torch.int32)
+    assert _status(lambda: dry.packed_prefill_attn(q, k, v, cu, 7)) == slm.SLM_OK
+    assert _status(lambda: dry.packed_prefill_attn(q, k, v, cu, 7, out_dtype=torch.bfloat16)) == slm.SLM_OK
+    # Hq % Hkv
+    assert _status(lambda: dry.packed_prefill_attn(_bf(10, 3, 64), k, v, cu, 7)) == slm.SLM_ERR_INVALID_ARG
+    # unsupported head dim
+    assert _status(lambda: dry.packed_prefill_attn(_bf(10, 4, 96), _bf(10, 2, 96), _bf(10, 2, 96), cu, 7)) \
+        == slm.SLM_ERR_UNSUPPORTED
+    # max_seqlen above T
+    assert _status(lambda: dry.packed_prefill_attn(q, k, v, cu, 11)) == slm.SLM_ERR_INVALID_ARG
+    # out aliasing q
+    out = q.view(torch.int16).view(torch.bfloat16).float()  # separate buffer, fine
+    assert _status(lambda: dry.packed_prefill_attn(q, k, v, cu, 7, out=out)) == slm.SLM_OK
+    big = torch.zeros(10 * 4 * 64 * 2, dtype=torch.bfloat16)
+    qa, oa = big[:2560].view(10, 4, 64), big[1280:1280 + 2560].view(10, 4, 64)
+    assert _status(lambda: dry.packed_prefill_attn(qa, k, v, cu, 7, out=oa, out_dtype=torch.bfloat16)) \
+        == slm.SLM_ERR_ALIAS
+    # empty pack is a no-op
+    e = _bf(0, 4, 64)
+    assert _status(lambda: dry.packed_prefill_attn(e, _bf(0, 2, 64), _bf(0, 2, 64),
+                                                   torch.zeros(1, dtype=torch.int32), 0)) == slm.SLM_OK
+
+
+def test_topk_validation(dry):
+    lp = torch.zeros((2, 3, 50), dtype=torch.float32)
+    cum = torch.zeros((2, 3), dtype=torch.float32)
+    assert _status(lambda: dry.beam_topk_merge(lp, cum, 4)) == slm.SLM_OK
+    assert _status(lambda: dry.beam_topk_merge(lp, cum, 151)) == slm.SLM_ERR_INVALID_ARG   # W > Win*V
+    assert _status(lambda: dry.beam_topk_merge(torch.zeros((2, 3, 500)), cum, 513)) == slm.SLM_ERR_UNSUPPORTED
+    small = slm.Context(device=-1, max_requests=1)
+    assert _status(lambda: small.beam_topk_merge(lp, cum, 4)) == slm.SLM_ERR_CAPACITY
+    buf = torch.zeros(2 * 3 * 50, dtype=torch.float32)
+    tok = buf[:8].view(torch.int32).view(2, 4)                  # overlaps logprobs
+    assert _status(lambda: dry.beam_topk_merge(buf.view(2, 3, 50), cum, 4, tokens=tok)) == slm.SLM_ERR_ALIAS
+
+
+def _beam_args(NL=2, R=2, W=3, P=5, S=4, Hq=4, Hkv=2, D=64):
+    return dict(q=_bf(NL, R, W, Hq, D), prefix_k=_bf(NL, R, P, Hkv, D), prefix_v=_bf(NL, R, P, Hkv, D),
+                suffix_k_in=_bf(NL, R, W, S, Hkv, D), suffix_v_in=_bf(NL, R, W, S, Hkv, D),
+                k_new=_bf(NL, R, W, Hkv, D), v_new=_bf(NL, R, W, Hkv, D),
+                parent=torch.zeros((R, W), dtype=torch.int32),
+                suffix_k_out=_bf(NL, R, W, S, Hkv, D), suffix_v_out=_bf(NL, R, W, S, Hkv, D))
+
+
+def test_decode_validation(dry):
+    a = _beam_args()
+    assert _status(lambda: dry.beam_decode_attn(hist_len=2, **a)) == slm.SLM_OK
+    assert _status(lambda: dry.beam_decode_attn(hist_len=4, **a)) == slm.SLM_ERR_INVALID_ARG  # hist+1 > S_cap
+    b = _beam_args(S=10)
+    assert _status(lambda: dry.beam_decode_attn(hist_len=8, **b)) == slm.SLM_ERR_UNSUPPORTED  # > 8 suffix rows
+    c = _beam_args(P=300, D=128)
+    assert _status(lambda: dry.beam_decode_attn(hist_len=1, **c)) == slm.SLM_ERR_UNSUPPORTED  # prompt beyond LDS
+    d = _beam_args(P=480, D=64)
+    assert _status(lambda: dry.beam_decode_attn(hist_len=1, **d)) == slm.SLM_OK
+    e = _beam_args()
+    e["suffix_k_out"] = e["suffix_k_in"]                          # in-place suffix update
+    assert _status(lambda: dry.beam_decode_attn(hist_len=1, **e)) == slm.SLM_ERR_ALIAS
+    f = _beam_args()
+    f["suffix_k_in"] = f["suffix_v_in"] = None
+    assert _status(lambda: dry.beam_decode_attn(hist_len=0, **f)) == slm.SLM_OK
+    assert _status(lambda: dry.beam_decode_attn(hist_len=1, **f)) == slm.SLM_ERR_INVALID_ARG
+
+
+def test_reorder_and_gather_validation(dry):
+    k = _bf(2, 2, 3, 4, 2, 64)
+    par = torch.zeros((2, 3), dtype=torch.int32)
+    assert _status(lambda: dry.beam_reorder_suffix(par, k, k.clone(), 2, _bf(2, 2, 3, 4, 2, 64),
+                                                   _bf(2, 2, 3, 4, 2, 64))) == slm.SLM_OK
+    assert _status(lambda: dry.beam_reorder_suffix(par, k, k.clone(), 5, _bf(2, 2, 3, 4, 2, 64),
+                                                   _bf(2, 2, 3, 4, 2, 64))) == slm.SLM_ERR_INVALID_ARG
+    assert _status(lambda: dry.beam_reorder_suffix(par, k, k.clone(), 2, k, _bf(2, 2, 3, 4, 2, 64))) \
+        == slm.SLM_ERR_ALIAS
+    hidden = _bf(10, 32)
+    cu = torch.tensor([0, 4, 10], dtype=torch.int32)
+    assert _status(lambda: dry.gather_last(hidden, cu)) == slm.SLM_OK
+    assert _status(lambda: dry.gather_last(hidden, cu, out=hidden[:2])) == slm.SLM_ERR_ALIAS
