@@ -1,0 +1,326 @@
+"""Benchmark of the bounded-generation attention hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input
+resident in HBM:
+  * prefill-only batch: 64 requests x 15 samples = 960 packed sequences
+    (lengths uniform on [64,500], T = 269,924 tokens), 28 layer calls of
+    packed causal GQA attention (16 query / 8 KV heads, head_dim 128, fp32
+    out) over one seeded Q/K/V set, then the last-valid-token gather of a
+    [T,1024] bf16 hidden state;
+  * short-prompt beam search: 32 requests x 100 beams, prompt 128, 4 fixed
+    decode steps over 24 layers (14 query / 2 KV heads, head_dim 64), vocab
+    151,936: first merge (one beam in), then per step the 24-layer decode
+    attention (history read through the last parents, suffix written in the
+    new order) and the top-k merge; finally the suffix reorder by the last
+    parents.
+
+value = prefill tokens per step (T, each through all 28 layers) / step time.
+The JSON line also carries the per-part times, the roofline of the dominant
+kernel (packed prefill attention) and the oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "packed-prefill attn tokens/s & beam-step µs; % of MFMA peak / HBM peak"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the timed oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def src_sha(name: str) -> str:
+    with open(os.path.join(ROOT, "bounded_generation_slm_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def prefill_bytes_flops(lengths, Hq, Hkv, D, out_bytes):
+    """Algorithmic bytes (q, k, v read once, out written once) and causal flops."""
+    T = sum(lengths)
+    byts = T * (Hq * D * 2 + 2 * Hkv * D * 2 + Hq * D * out_bytes)
+    flops = 2 * Hq * D * sum(L * (L + 1) for L in lengths)    # QK^T and PV over causal pairs
+    return byts, flops
+
+
+def decode_bytes(s, t):
+    """Algorithmic bytes of the 24-layer decode attention at step t (s = t rows)."""
+    NL, R, W, P, Hq, Hkv, D = s.n_layers, s.num_requests, s.width, s.prompt_len, s.n_heads_q, s.n_heads_kv, s.head_dim
+    q = NL * R * W * Hq * D * 2
+    prompt = NL * R * P * Hkv * D * 2 * 2
+    suffix = 2 * NL * R * W * t * Hkv * D * 2 * 2          # read t rows (history + new), write t rows
+    out = NL * R * W * Hq * D * 4
+    return q + prompt + suffix + out
+
+
+def topk_bytes(R, Win, V, W):
+    return R * Win * V * 4 + R * Win * 4 + R * W * 12
+
+
+def cpu_baseline(pf, bs):
+    """The oracle on a bounded sample of the same workload, scaled to the whole
+    step: 1/4 of the prefill sequences (one layer), one layer of each decode
+    step, and 4 requests of each merge."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    L = list(pf.lengths)
+    sub = L[::4]
+    shp = wl.PrefillShape("sample", pf.base_seed, tuple(sub), pf.n_heads_q, pf.n_heads_kv, pf.head_dim)
+    x = wl.prefill_inputs(shp)
+    t0 = time.perf_counter()
+    oracle.prefill_attn(x["q"], x["k"], x["v"], x["cu_seqlens"])
+    t_pre = time.perf_counter() - t0
+    pairs = lambda ls: sum(l * (l + 1) for l in ls)
+    est = t_pre * pairs(L) / pairs(sub) * pf.n_layers
+
+    st = wl.beam_static_inputs(bs, layers=[0])
+    hist_rng = np.random.default_rng(0)
+    t_dec = 0.0
+    for t in range(1, bs.n_steps + 1):
+        xs = wl.beam_step_inputs(bs, t, layers=[0])
+        shp6 = (1, bs.num_requests, bs.width, bs.suffix_cap, bs.n_heads_kv, bs.head_dim)
+        sk = wl.f32_to_bf16_bits(hist_rng.standard_normal(shp6).astype(np.float32))
+        par = hist_rng.integers(0, bs.width, size=(bs.num_requests, bs.width)).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.beam_decode_attn(xs["q"], st["prefix_k"], st["prefix_v"], sk, sk, xs["k_new"], xs["v_new"], par, t - 1)
+        t_dec += time.perf_counter() - t0
+    est += t_dec * bs.n_layers
+
+    r_s = 4
+    t_top = 0.0
+    for t in range(0, bs.n_steps + 1):
+        win = 1 if t == 0 else bs.width
+        lp = wl.logprobs(bs.base_seed, (r_s, win, bs.vocab), t)
+        cum = np.zeros((r_s, win), np.float32)
+        t0 = time.perf_counter()
+        oracle.topk_merge(lp, cum, bs.width)
+        t_top += time.perf_counter() - t0
+    est += t_top * bs.num_requests / r_s
+    sampled = t_pre + t_dec + t_top
+    return {
+        "value": pf.total_tokens / est,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": ("fp64 C oracle, %d threads: prefill layer 0 over %d of 960 sequences (%d tokens), "
+                   "decode layer 0 of each of the 4 steps, top-k merge of 4 of 32 requests for the 5 merges; "
+                   "%.1f s measured, scaled by causal pairs / layers / requests to one whole step "
+                   "(%.0f s estimated)" % (threads, len(sub), sum(sub), sampled, est)),
+    }
+
+
+def traffic_from_counters(kernel_file: str, launch_bytes_key: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source."""
+    path = os.path.join(PROFILES, "prefill_attn_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha") != src_sha(kernel_file):
+        return None
+    return rec.get(launch_bytes_key)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the path shards by sequence / request "
+              "with no exchange); --gpus %d is not run" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bounded_generation_slm_amd as slm
+    import workloads as wl
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = 1 << 28                                  # 1 GiB of fp32
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 3}))
+        return
+
+    ctx = slm.Context(0)
+    pf, bs = wl.PREFILL_THROUGHPUT, wl.BEAM_SHORT
+
+    # ---- inputs, resident in HBM before timing ----
+    T, Hq, Hkv, D = pf.total_tokens, pf.n_heads_q, pf.n_heads_kv, pf.head_dim
+    q = wl.torch_normal_bf16((T, Hq, D), (pf.base_seed, wl.TID_Q, 0, 0), dev)
+    k = wl.torch_normal_bf16((T, Hkv, D), (pf.base_seed, wl.TID_K, 0, 0), dev)
+    v = wl.torch_normal_bf16((T, Hkv, D), (pf.base_seed, wl.TID_V, 0, 0), dev)
+    hidden = wl.torch_normal_bf16((T, pf.hidden_dim), (pf.base_seed, wl.TID_HIDDEN, 0, 0), dev)
+    cu = torch.from_numpy(pf.cu_seqlens()).to(dev)
+    pout = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+    gout = torch.empty((len(pf.lengths), pf.hidden_dim), dtype=torch.bfloat16, device=dev)
+
+    NL, R, W, P, N, V = bs.n_layers, bs.num_requests, bs.width, bs.prompt_len, bs.n_steps, bs.vocab
+    bHq, bHkv, bD = bs.n_heads_q, bs.n_heads_kv, bs.head_dim
+    pk = wl.torch_normal_bf16((NL, R, P, bHkv, bD), (bs.base_seed, wl.TID_PREFIX_K, 0, 0), dev)
+    pv = wl.torch_normal_bf16((NL, R, P, bHkv, bD), (bs.base_seed, wl.TID_PREFIX_V, 0, 0), dev)
+    bq = [None] + [wl.torch_normal_bf16((NL, R, W, bHq, bD), (bs.base_seed, wl.TID_Q, 0, t), dev) for t in range(1, N + 1)]
+    kn = [None] + [wl.torch_normal_bf16((NL, R, W, bHkv, bD), (bs.base_seed, wl.TID_K_NEW, 0, t), dev) for t in range(1, N + 1)]
+    vn = [None] + [wl.torch_normal_bf16((NL, R, W, bHkv, bD), (bs.base_seed, wl.TID_V_NEW, 0, t), dev) for t in range(1, N + 1)]
+    lps = [wl.torch_logprobs((R, 1 if t == 0 else W, V), (bs.base_seed, wl.TID_LOGITS, 0, t), dev) for t in range(N + 1)]
+    cum0 = torch.zeros((R, 1), dtype=torch.float32, device=dev)
+    toks = [torch.empty((R, W), dtype=torch.int32, device=dev) for _ in range(N + 1)]
+    pars = [torch.empty((R, W), dtype=torch.int32, device=dev) for _ in range(N + 1)]
+    cums = [torch.empty((R, W), dtype=torch.float32, device=dev) for _ in range(N + 1)]
+    sshape = (NL, R, W, bs.suffix_cap, bHkv, bD)
+    suf = [(torch.zeros(sshape, dtype=torch.bfloat16, device=dev), torch.zeros(sshape, dtype=torch.bfloat16, device=dev))
+           for _ in range(3)]
+    bout = torch.empty((NL, R, W, bHq, bD), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def step(marks):
+        """One pass of the whole hot path; marks collects (part, start, end) events."""
+        for _ in range(pf.n_layers):
+            e0 = ev()
+            ctx.packed_prefill_attn(q, k, v, cu, pf.max_seqlen, out=pout)
+            marks.append(("prefill", e0, ev()))
+        e0 = ev()
+        ctx.gather_last(hidden, cu, out=gout)
+        marks.append(("gather", e0, ev()))
+        e0 = ev()
+        ctx.beam_topk_merge(lps[0], cum0, W, toks[0], pars[0], cums[0])
+        marks.append(("merge0", e0, ev()))
+        for t in range(1, N + 1):
+            (ski, svi), (sko, svo) = suf[(t + 1) % 2], suf[t % 2]
+            e0 = ev()
+            ctx.beam_decode_attn(bq[t], pk, pv, ski if t > 1 else None, svi if t > 1 else None, kn[t], vn[t],
+                                 pars[t - 1], t - 1, sko, svo, out=bout)
+            e1 = ev()
+            ctx.beam_topk_merge(lps[t], cums[t - 1], W, toks[t], pars[t], cums[t])
+            e2 = ev()
+            marks.append(("decode%d" % t, e0, e1))
+            marks.append(("merge%d" % t, e1, e2))
+        e0 = ev()
+        ctx.beam_reorder_suffix(pars[N], suf[N % 2][0], suf[N % 2][1], N, suf[2][0], suf[2][1])
+        marks.append(("reorder", e0, ev()))
+
+    for _ in range(args.warmup):
+        step([])
+    ctx.check()
+    torch.cuda.synchronize()
+
+    marks = []
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step(marks)
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ctx.check()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+
+    per = {}
+    for name, a, b in marks:
+        per.setdefault(name, []).append(a.elapsed_time(b) * 1e3)   # us
+    avg = {kk: sum(vv) / len(vv) for kk, vv in per.items()}
+    prefill_us = avg["prefill"]
+    beam_parts = ["merge0"] + ["decode%d" % t for t in range(1, N + 1)] + ["merge%d" % t for t in range(1, N + 1)] + ["reorder"]
+    beam_search_us = sum(avg[p] for p in beam_parts)
+    step_us = [avg["decode%d" % t] + avg["merge%d" % t] for t in range(1, N + 1)]
+
+    pbytes, pflops = prefill_bytes_flops(pf.lengths, Hq, Hkv, D, 4)
+    achieved_gbs = pbytes / (prefill_us * 1e-6) / 1e9
+    mfma_tflops = pflops / (prefill_us * 1e-6) / 1e12
+    step_bytes = [decode_bytes(bs, t) + topk_bytes(R, W, V, W) for t in range(1, N + 1)]
+    step_gbs = [b / (u * 1e-6) / 1e9 for b, u in zip(step_bytes, step_us)]
+    traffic = traffic_from_counters("prefill_attn.hip", "hbm_bytes_per_launch")
+
+    value = pf.total_tokens / (ms_step * 1e-3)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill_throughput (960 packed seqs, T=%d, 28 layers, Hq16/Hkv8/D128, fp32 out) + gather "
+                        "[T,1024]; beam_short_prompt (R32 x W100, P128, 4 steps, 24 layers, Hq14/Hkv2/D64, V151936)"
+                        % T,
+            "value_counts": "prefill tokens per step (each through 28 layers) / whole-step time",
+        },
+        "roofline": {
+            "kernel": "prefill_attn_kernel<128,2,f32>",
+            "bound": "hbm",
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": pbytes,
+            "avg_launch_us": round(prefill_us, 2),
+            "mfma_tflops_causal": round(mfma_tflops, 1),
+            "mfma_frac": round(mfma_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "mfma_frac_ceiling_at_hbm_peak": round(min(1.0, pflops / pbytes * HBM_PEAK_GBS * 1e9 / 1e12
+                                                       / MFMA_BF16_PEAK_TFLOPS), 4),
+        },
+        "parts": {
+            "prefill_layer_us": round(prefill_us, 2),
+            "prefill_28_layers_ms": round(prefill_us * pf.n_layers / 1e3, 3),
+            "prefill_tokens_per_s": round(pf.total_tokens / (prefill_us * pf.n_layers * 1e-6), 1),
+            "gather_us": round(avg["gather"], 2),
+            "beam_search_us": round(beam_search_us, 1),
+            "beam_step_us": [round(u, 1) for u in step_us],
+            "beam_step_us_mean": round(sum(step_us) / N, 1),
+            "beam_step_hbm_frac": [round(g / HBM_PEAK_GBS, 4) for g in step_gbs],
+            "decode_us": [round(avg["decode%d" % t], 1) for t in range(1, N + 1)],
+            "merge_us": [round(avg["merge%d" % t], 1) for t in range(0, N + 1)],
+            "reorder_us": round(avg["reorder"], 1),
+            "beam_requests_per_s": round(R / (beam_search_us * 1e-6), 1),
+            "host_wall_s": round(t_wall, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(pf, bs)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
