@@ -81,11 +81,18 @@ struct TopkParams {
     int32_t* tokens;
     int32_t* parent;
     float* cum_out;
-    uint64_t* stage1;                   // workspace: [R, Win, even(W)] keys, 0 = empty
+    uint64_t* stage1;                   // workspace: [R, list_cap] appended stage-1 keys
+    uint64_t* req_thr;                  // workspace: [R] shared thresholds, zero between calls
+    int* req_cnt;                       // workspace: [R] appended key counts, zero between calls
+    int64_t list_cap;                   // keys per request list (>= Win * chunks * W)
     int num_requests, beams_in, vocab, width;
+    int chunks, chunk_len;              // vocabulary chunks per row and their length
 };
 hipError_t launch_beam_topk_merge(const TopkParams& p, hipStream_t stream);
 size_t beam_topk_workspace_bytes(int max_requests, int max_beams);
+int beam_topk_chunks(int num_requests, int beams_in, int vocab, int max_chunks);
+constexpr int kTopkMinItems = 2048;     // stage-1 waves a call aims for
+constexpr int kTopkMaxChunks = 64;      // vocabulary chunks per row at most
 size_t beam_decode_lds_bytes(int head_dim, int prompt_len);
 constexpr int kTopkMaxWidth = 512;
 constexpr int kDecodeMaxSuffix = 8;     // hist_len + 1 <= 8

@@ -24,8 +24,9 @@ struct slm_ctx {
     bool dry_run = false;   // device < 0: validate arguments only, touch no device
     hipStream_t stream = nullptr;
     slm_caps caps{};
-    uint64_t* topk_ws = nullptr;
+    uint64_t* topk_ws = nullptr;    // [R] shared thresholds, [R] counts (8 B slots), [R] key lists
     size_t topk_ws_bytes = 0;
+    int64_t topk_lists = 0;         // stage-1 lists (of up to max_beams keys) per request
     int* err_flag = nullptr;
     size_t max_lds = 0;
     char last_error[512] = {0};
@@ -133,9 +134,12 @@ slm_status slm_ctx_create(int device, const slm_caps* caps, slm_ctx** out) {
     }
     ctx->max_lds = prop.sharedMemPerBlock;
     ctx->topk_ws_bytes = slm::beam_topk_workspace_bytes(c.max_requests, c.max_beams);
+    ctx->topk_lists = std::max<int64_t>((int64_t)c.max_beams, slm::kTopkMaxChunks);
     if (hipMalloc((void**)&ctx->topk_ws, ctx->topk_ws_bytes) != hipSuccess ||
+        hipMemset(ctx->topk_ws, 0, ctx->topk_ws_bytes) != hipSuccess ||
         hipMalloc((void**)&ctx->err_flag, sizeof(int)) != hipSuccess ||
-        hipMemset(ctx->err_flag, 0, sizeof(int)) != hipSuccess) {
+        hipMemset(ctx->err_flag, 0, sizeof(int)) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
         if (ctx->topk_ws) (void)hipFree(ctx->topk_ws);
         if (ctx->err_flag) (void)hipFree(ctx->err_flag);
         delete ctx;
@@ -336,7 +340,17 @@ slm_status slm_beam_topk_merge(slm_ctx* ctx, const float* logprobs, const float*
         return fail(ctx, SLM_ERR_ALIAS, "topk: outputs overlap each other");
     slm::TopkParams p{};
     p.logprobs = logprobs; p.cum = cum; p.tokens = tokens; p.parent = parent; p.cum_out = cum_out;
-    p.stage1 = ctx->topk_ws; p.num_requests = num_requests; p.beams_in = beams_in; p.vocab = vocab; p.width = width;
+    const int64_t R_cap = ctx->caps.max_requests;
+    p.req_thr = ctx->topk_ws;
+    p.req_cnt = (int*)(ctx->topk_ws + R_cap);
+    p.stage1 = ctx->topk_ws + 2 * R_cap;
+    p.list_cap = ctx->topk_lists * ctx->caps.max_beams;
+    p.num_requests = num_requests; p.beams_in = beams_in; p.vocab = vocab; p.width = width;
+    // lists per request = beams_in * chunks must fit the per-request capacity
+    int chunks = slm::beam_topk_chunks(num_requests, beams_in, vocab,
+                                       (int)std::min<int64_t>(ctx->topk_lists / beams_in, INT32_MAX));
+    p.chunk_len = ((vocab + chunks - 1) / chunks + 3) & ~3;
+    p.chunks = (vocab + p.chunk_len - 1) / p.chunk_len;
     return SLM_LAUNCH(ctx, slm::launch_beam_topk_merge(p, ctx->stream), "topk");
 }
 
