@@ -43,7 +43,8 @@ EXPORTED = (
 
 class _Caps(ctypes.Structure):
     _fields_ = [("max_requests", ctypes.c_int32), ("max_beams", ctypes.c_int32),
-                ("max_vocab", ctypes.c_int32)]
+                ("max_vocab", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+                ("max_seqs", ctypes.c_int32), ("max_heads_q", ctypes.c_int32)]
 
 
 class _BeamAttnArgs(ctypes.Structure):
@@ -112,20 +113,22 @@ class Context:
     host-side validation on CPU tensors and launches nothing."""
 
     def __init__(self, device: int = 0, max_requests: int = 64, max_beams: int = 512,
-                 max_vocab: int = 262144):
+                 max_vocab: int = 262144, max_tokens: int = 1 << 20, max_seqs: int = 8192,
+                 max_heads_q: int = 64):
         self.dry_run = device < 0
         if self.dry_run:
             self.device = torch.device("cpu")
         else:
             self.device = torch.device("cuda", device)
             torch.cuda.init()
-        caps = _Caps(max_requests, max_beams, max_vocab)
+        caps = _Caps(max_requests, max_beams, max_vocab, max_tokens, max_seqs, max_heads_q)
         handle = _P()
         rc = _lib.slm_ctx_create(device, ctypes.byref(caps), ctypes.byref(handle))
         if rc != SLM_OK:
             raise SlmError(rc, "slm_ctx_create(device=%d)" % device)
         self._h = handle
-        self.caps = dict(max_requests=max_requests, max_beams=max_beams, max_vocab=max_vocab)
+        self.caps = dict(max_requests=max_requests, max_beams=max_beams, max_vocab=max_vocab,
+                         max_tokens=max_tokens, max_seqs=max_seqs, max_heads_q=max_heads_q)
 
     def close(self):
         if getattr(self, "_h", None):

@@ -28,9 +28,19 @@ struct PrefillParams {
     int q_tiles;                        // query tiles per sequence (from max_seqlen)
     int n_units;                        // num_seqs * Hkv * head_blocks
     float scale_log2;                   // softmax scale * log2(e)
+    // plan workspace (persistent form): work units per XCD
+    int4* plan_items;                   // {s0, L, unit in sequence, query tile}
+    int* plan_count;                    // [8] units per XCD
+    int* plan_off;                      // [8] first unit of each XCD in plan_items
+    int* plan_claim;                    // [8] per-XCD item counters (zeroed by the plan kernel)
+    int plan_cap;                       // capacity of plan_items
 };
-hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, bool out_bf16,
-                               hipStream_t stream);
+hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, bool out_bf16, bool persistent,
+                               int num_cus, hipStream_t stream);
+// plan entries a pack can need: sum over sequences of ceil(L / qt_rows), per unit column
+inline int64_t prefill_plan_entries(int64_t max_tokens, int64_t max_seqs, int64_t max_heads_q) {
+    return max_tokens * max_heads_q / 128 + max_seqs * max_heads_q;
+}
 
 struct GatherParams {
     const void* hidden;

@@ -4,10 +4,10 @@
 // "Packed Prefill" and §1.2): sequences are packed back to back with no
 // padding; each query attends causally to the keys of its own sequence only.
 //
-// Work decomposition: a workgroup (4 waves) owns one (sequence, KV head, block
-// of query heads of that group, query tile).  The query heads of one GQA group
-// share every K/V tile staged in LDS.  Each wave owns 32 query rows of one
-// head and runs the online softmax in registers:
+// Work unit: one (sequence, KV head, block of query heads of that group,
+// query tile), processed by a workgroup of 4 waves.  The query heads of one
+// GQA group share every K/V tile staged in LDS.  Each wave owns 32 query rows
+// of one head and runs the online softmax in registers:
 //   S^T = K Q^T   (v_mfma_f32_32x32x16_bf16, K from LDS, Q^T in VGPRs)
 //   O^T += V^T P^T
 // Computing S transposed puts each lane on one query column, so the row max
@@ -21,10 +21,14 @@
 // V stays row-major; its V^T operand comes from ds_read_b64_tr_b16, whose
 // 16-lane transpose hands each lane one d column of four keys.
 //
-// Grid mapping is XCD-aware: the query tiles of one (sequence, head block)
-// are consecutive on one XCD (blockIdx % 8), so the K/V rows they share are
-// fetched from HBM once and re-read from that XCD's L2.  Heavier tiles (later
-// query tiles, which see more keys) are dispatched first within a unit.
+// Two launch forms share the per-tile code:
+//   * one workgroup per work unit (small packs), XCD-aware block order;
+//   * for large packs, a plan kernel lists the non-empty work units per XCD
+//     (the units of one (sequence, head block) on one XCD so they share its
+//     L2, heavier query tiles first), and persistent workgroups walk their
+//     XCD's list as one continuous K/V tile stream: the next unit's first
+//     tiles and its Q rows are in flight while the current unit finishes,
+//     and each unit's output leaves through unconditional buffer stores.
 #include <type_traits>
 
 #include "common.h"
@@ -33,8 +37,6 @@
 namespace slm {
 namespace {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
@@ -47,34 +49,279 @@ __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
-// s_waitcnt lgkmcnt(0) only
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14)); }
+// s_waitcnt with only an lgkmcnt limit
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (N << 8) | (0x3 << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() { wait_lgkm<0>(); }
+// Registers filled by the inline-asm loads below are invisible to the
+// compiler's dependency tracking: it may move their (side-effect free)
+// consumers such as MFMAs above the wait that guards them.  Passing each such
+// register through an empty volatile asm after the wait pins the order.
+template <class T>
+__device__ __forceinline__ void pin_after_wait(T& x) {
+    asm volatile("" : "+v"(x));
+}
 
-// ds_read_b64_tr_b16 issued directly, with a compile-time byte offset: the
-// compiler neither tracks nor waits for it, so the caller waits with
-// wait_lgkm0() before using the result.  (Through the builtin, the compiler
-// would also wait for every in-flight direct-to-LDS load of later tiles.)
+// Memory operations issued directly: the compiler neither tracks nor waits
+// for them, so every use is preceded by an explicit wait.  (The compiler would
+// otherwise wait for all in-flight direct-to-LDS loads before each LDS access
+// it cannot disambiguate, draining the tile pipeline.)
 template <int OFF>
 __device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
     u32x2 r;
     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
     return r;
 }
+__device__ __forceinline__ void lds_write16(uint32_t addr, u32x4 v) {
+    asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read16_at(uint32_t addr) {
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+    return r;
+}
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+    return r;
+}
+__device__ __forceinline__ u32x4 global_load16(const void* p) {
+    u32x4 r;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
+// A wave-uniform 16-byte entry through the scalar cache, waited for at once.
+__device__ __forceinline__ int4 scalar_load16(const int4* p) {
+    int4 r;
+    asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
+    return r;
+}
+__device__ __forceinline__ int scalar_load4(const int* p) {
+    int r;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
+    return r;
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
 
+template <int D>
+struct Geo {
+    static constexpr int NKS = D / 16;          // k-steps of S^T over the head dim
+    static constexpr int NDB = D / 32;          // 32-row blocks of O^T
+    static constexpr int ROWB = D * 2;          // bytes of one K/V row in LDS
+    static constexpr int CPR = D / 8;           // 16-byte chunks per row
+    static constexpr int TILEB = kKT * ROWB;    // bytes of one K (or V) tile
+    static constexpr int STAGEB = 2 * TILEB;    // K tile then V tile
+    static constexpr int LPW = TILEB / 1024 / 4;    // direct loads per wave per K (or V) tile
+    static_assert(LPW >= 1, "tile too small for 4 waves");
+};
+
+// Per-lane offsets that do not depend on the work unit.
+template <int D>
+struct LaneConst {
+    int koff[Geo<D>::NKS];                      // K operand, per k-step
+    uint32_t voff[Geo<D>::NDB];                 // V^T transpose reads (k-step 0, first read)
+    int dma_r[Geo<D>::LPW], dma_ck[Geo<D>::LPW], dma_cv[Geo<D>::LPW];
+};
+
+// K row r keeps its 16-byte chunk c at position c ^ (r % CPR); V row r keeps
+// chunk c at position c ^ (2 * (r % 4)), so transpose reads of four
+// consecutive rows hit distinct banks.
+template <int D>
+__device__ __forceinline__ void make_lane_const(LaneConst<D>& lc, int lane, int wave, uint32_t ring_base) {
+    using G = Geo<D>;
+    const int n = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < G::NKS; ++ks) lc.koff[ks] = ring_base + n * G::ROWB + (((2 * ks + hf) ^ (n % G::CPR)) * 16);
+    // V^T operand of k-step j, d-block db: in each 16-lane group, lane r
+    // points at 4 d's of key ka (first read) or ka + 8 (second read) and
+    // receives its own d column of four keys.  Those keys are 16j + 8(e/4) +
+    // 4hf + e%4, the keys the P^T operand of the same k-step holds.  The
+    // swizzle term depends on ka % 4 only, which neither j (16 keys) nor the
+    // second read (8 keys) changes, so those steps are constant offsets.
+    const int grp = lane >> 4, r = lane & 15;
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+        const int dcol = db * 32 + 16 * (grp & 1) + 4 * (r & 3);
+        const int chunk = dcol / 8, within = (dcol % 8) * 2;
+        const int ka = 4 * (grp >> 1) + (r >> 2);
+        lc.voff[db] = ring_base + G::TILEB + ka * G::ROWB + ((chunk ^ (2 * (ka & 3))) * 16) + within;
+    }
+#pragma unroll
+    for (int i = 0; i < G::LPW; ++i) {
+        const int byte = (wave * G::LPW + i) * 1024 + lane * 16;
+        lc.dma_r[i] = byte / G::ROWB;
+        const int pos = (byte % G::ROWB) / 16;
+        lc.dma_ck[i] = (pos ^ (lc.dma_r[i] % G::CPR)) * 8;
+        lc.dma_cv[i] = (pos ^ (2 * (lc.dma_r[i] & 3))) * 8;
+    }
+}
+
+// Direct loads of one tile into stage STAGE: each wave writes LPW contiguous
+// KiB of K and of V (2 * LPW vector-memory instructions).  Rows past the
+// sequence re-read its last row (finite values; every such key is masked).
+template <int D, int STAGE>
+__device__ __forceinline__ void issue_tile(char* ring, const LaneConst<D>& lc, const uint16_t* kbase,
+                                           const uint16_t* vbase, int64_t kv_stride, int k0, int L, int wave) {
+    using G = Geo<D>;
+#pragma unroll
+    for (int i = 0; i < G::LPW; ++i) {
+        const int64_t row = (int64_t)min(k0 + lc.dma_r[i], L - 1) * kv_stride;
+        char* kdst = ring + STAGE * G::STAGEB + (wave * G::LPW + i) * 1024;
+        __builtin_amdgcn_global_load_lds((glb_void*)(kbase + row + lc.dma_ck[i]), (lds_void*)kdst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((glb_void*)(vbase + row + lc.dma_cv[i]), (lds_void*)(kdst + G::TILEB), 16, 0, 0);
+    }
+}
+
+// One 32-key tile: S^T = K Q^T, online softmax (running max m in raw score
+// units, scale folded into exp2), O^T += V^T P^T.
+template <int D, int STAGE, bool MASK>
+__device__ __forceinline__ void attend_tile(const char* ring, const LaneConst<D>& lc,
+                                            const u32x4 (&qreg)[Geo<D>::NKS], int k0, int qrow, int hf, float c,
+                                            float& m, float& lsum, f32x16 (&o)[Geo<D>::NDB], bool diag = true) {
+    using G = Geo<D>;
+    constexpr int H = G::NKS / 2;
+    f32x16 sacc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+    u32x4 ka[G::NKS];                           // K operand rows, read in two halves
+#pragma unroll
+    for (int ks = 0; ks < G::NKS; ++ks) ka[ks] = lds_read16_at<STAGE * G::STAGEB>(lc.koff[ks]);
+    wait_lgkm<H>();
+#pragma unroll
+    for (int ks = 0; ks < H; ++ks) {
+        pin_after_wait(ka[ks]);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[ks]), as_bf16x8(qreg[ks]), sacc, 0, 0, 0);
+    }
+    wait_lgkm0();
+#pragma unroll
+    for (int ks = H; ks < G::NKS; ++ks) {
+        pin_after_wait(ka[ks]);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[ks]), as_bf16x8(qreg[ks]), sacc, 0, 0, 0);
+    }
+    u32x2 vop[G::NDB][2];                       // V^T operands of k-step 0, read while the softmax runs
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+        vop[db][0] = lds_read_tr16<STAGE * G::STAGEB>(lc.voff[db]);
+        vop[db][1] = lds_read_tr16<STAGE * G::STAGEB + 8 * G::ROWB>(lc.voff[db]);
+    }
+    if (MASK && diag) {                         // tile reaches past this wave's first row: causal mask
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (k0 + 8 * (i >> 2) + 4 * hf + (i & 3) > qrow) sacc[i] = -INFINITY;
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[i]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mnew = fmaxf(m, tmax);          // finite: key 0 is in tile 0 for every row
+    if (__ballot(mnew > m) != 0) {              // rescale only when some running max moved
+        const float alpha = fast_exp2((m - mnew) * c);
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        m = mnew;
+    }
+    const float mc = m * c;
+    float psum = 0.f;
+    uint32_t pk[8];
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+        const float p0 = fast_exp2(fmaf(sacc[i], c, -mc)), p1 = fast_exp2(fmaf(sacc[i + 1], c, -mc));
+        psum += p0 + p1;
+        pk[i >> 1] = pack_bf16x2(p0, p1);
+    }
+    lsum += psum;
+    wait_lgkm0();                               // the transpose reads have landed
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+        pin_after_wait(vop[db][0]);
+        pin_after_wait(vop[db][1]);
+    }
+    {
+        const u32x4 pb = {pk[0], pk[1], pk[2], pk[3]};
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) {
+            const u32x4 a = {vop[db][0][0], vop[db][0][1], vop[db][1][0], vop[db][1][1]};
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pb), o[db], 0, 0, 0);
+            vop[db][0] = lds_read_tr16<STAGE * G::STAGEB + 16 * G::ROWB>(lc.voff[db]);   // k-step 1
+            vop[db][1] = lds_read_tr16<STAGE * G::STAGEB + 24 * G::ROWB>(lc.voff[db]);
+        }
+    }
+    wait_lgkm0();
+#pragma unroll
+    for (int db = 0; db < G::NDB; ++db) {
+        pin_after_wait(vop[db][0]);
+        pin_after_wait(vop[db][1]);
+    }
+    {
+        const u32x4 pb = {pk[4], pk[5], pk[6], pk[7]};
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db) {
+            const u32x4 a = {vop[db][0][0], vop[db][0][1], vop[db][1][0], vop[db][1][1]};
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pb), o[db], 0, 0, 0);
+        }
+    }
+}
+
+// Epilogue geometry: each wave stages its 32 x D block through LDS in passes
+// of PCOLS columns (rows padded by 16 bytes), then stores whole contiguous
+// row segments.
+template <int D, bool OUT_BF16>
+struct Epi {
+    static constexpr int OB = OUT_BF16 ? 2 : 4;             // output bytes per element
+    static constexpr int PCOLS = 32;                        // columns per pass
+    static constexpr int PROWB = PCOLS * OB + 16;           // padded LDS row bytes
+    static constexpr int WAVEB = 32 * PROWB;                // LDS bytes per wave
+    static constexpr int CH = PCOLS * OB / 16;              // 16-byte chunks per row segment
+    static constexpr int NPASS = D / PCOLS;
+    static constexpr int SPP = 32 * CH / 64;                // stores per lane per pass
+    static constexpr int NST = NPASS * SPP;                 // stores per lane per unit
+};
+
+// Normalised rows of one wave into its LDS staging block (pass `pass`).
+template <int D, bool OUT_BF16>
+__device__ __forceinline__ void epi_stage(uint32_t wbuf, const f32x16 (&o)[Geo<D>::NDB], float inv, int pass,
+                                          int n, int hf) {
+    using E = Epi<D, OUT_BF16>;
+#pragma unroll
+    for (int dbp = 0; dbp < E::PCOLS / 32; ++dbp) {
+        const int db = pass * (E::PCOLS / 32) + dbp;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const int col = dbp * 32 + 8 * i4 + 4 * hf;
+            const float r0 = o[db][4 * i4] * inv, r1 = o[db][4 * i4 + 1] * inv;
+            const float r2 = o[db][4 * i4 + 2] * inv, r3 = o[db][4 * i4 + 3] * inv;
+            const uint32_t a = wbuf + n * E::PROWB + col * E::OB;
+            if constexpr (OUT_BF16) {
+                const u32x2 v = {pack_bf16x2(r0, r1), pack_bf16x2(r2, r3)};
+                asm volatile("ds_write_b64 %0, %1" : : "v"(a), "v"(v) : "memory");
+            } else {
+                lds_write16(a, u32x4{__builtin_bit_cast(uint32_t, r0), __builtin_bit_cast(uint32_t, r1),
+                                     __builtin_bit_cast(uint32_t, r2), __builtin_bit_cast(uint32_t, r3)});
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One workgroup per work unit.
 template <int D, int NH, bool OUT_BF16>
 __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(const PrefillParams p) {
+    using G = Geo<D>;
+    using E = Epi<D, OUT_BF16>;
     constexpr int QT = 128 / NH;        // query rows per workgroup
     constexpr int WPH = 4 / NH;         // waves per query head
-    constexpr int NKS = D / 16;         // k-steps of S^T over the head dim
-    constexpr int NDB = D / 32;         // 32-row blocks of O^T
-    constexpr int ROWB = D * 2;         // bytes of one K/V row in LDS
-    constexpr int CPR = D / 8;          // 16-byte chunks per row
-    constexpr int TILEB = kKT * ROWB;   // bytes of one K (or V) tile
-    constexpr int STAGEB = 2 * TILEB;   // K tile then V tile
-    constexpr int LPW = TILEB / 1024 / 4;   // direct loads per wave per K (or V) tile
-    static_assert(LPW >= 1, "tile too small for 4 waves");
+    static_assert(4 * E::WAVEB <= kStages * G::STAGEB, "epilogue staging must fit the ring");
 
-    __shared__ __attribute__((aligned(1024))) char lds[kStages * STAGEB];
+    __shared__ __attribute__((aligned(1024))) char ring[kStages * G::STAGEB];
 
     const int idx = blockIdx.x;
     const int xcd = idx % kNumXcd, slot = idx / kNumXcd;
@@ -101,151 +348,42 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(const PrefillParam
     const int h = g * p.group + hb * NH + wave / WPH;
     const int wrow0 = q0 + (wave % WPH) * 32;   // first query row of this wave
     const int qrow = wrow0 + n;                 // this lane's query row (in-sequence)
-    const int last_tile = min(wrow0 + 31, L - 1) / kKT;   // last tile with a visible key
+    const int last_tile = wrow0 < L ? min(wrow0 + 31, L - 1) / kKT : -1;   // last tile it needs
     const float c = p.scale_log2;
 
-    // Q^T operand: lane (n, hf) holds d = ks*16 + hf*8 .. +7 of query row n
-    u32x4 qreg[NKS];
+    u32x4 qreg[G::NKS];                         // Q^T: lane (n, hf) holds d = ks*16 + hf*8 .. +7
     {
         const uint16_t* qp = p.q + ((int64_t)(s0 + min(qrow, L - 1)) * p.n_heads_q + h) * D + hf * 8;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qreg[ks] = *(const u32x4*)(qp + ks * 16);
+        for (int ks = 0; ks < G::NKS; ++ks) qreg[ks] = *(const u32x4*)(qp + ks * 16);
     }
-
-    // Per-lane LDS byte offsets inside one stage.  K row r keeps its 16-byte
-    // chunk c at position c ^ (r % CPR); V row r keeps chunk c at position
-    // c ^ (2 * (r % 4)), so transpose reads of four consecutive rows hit
-    // distinct banks.
-    int koff[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) koff[ks] = n * ROWB + (((2 * ks + hf) ^ (n % CPR)) * 16);
-    // V^T operand of k-step j, d-block db: in each 16-lane group, lane r
-    // points at 4 d's of key ka (first read) or ka + 8 (second read) and
-    // receives its own d column of four keys.  Those keys are 16j + 8(e/4) +
-    // 4hf + e%4, the keys the P^T operand of the same k-step holds.
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
-    uint32_t voff[2][NDB][2];
-    {
-        const int grp = lane >> 4, r = lane & 15;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const int dcol = db * 32 + 16 * (grp & 1) + 4 * (r & 3);
-                const int chunk = dcol / 8, within = (dcol % 8) * 2;
-                const int ka = 16 * j + 4 * (grp >> 1) + (r >> 2), kb2 = ka + 8;
-                voff[j][db][0] = lds_base + TILEB + ka * ROWB + ((chunk ^ (2 * (ka & 3))) * 16) + within;
-                voff[j][db][1] = lds_base + TILEB + kb2 * ROWB + ((chunk ^ (2 * (kb2 & 3))) * 16) + within;
-            }
-    }
-    // Direct loads of one tile: each wave writes LPW contiguous KiB of K and of
-    // V.  Rows past the sequence re-read its last row (finite values; every
-    // such key is masked).
+    LaneConst<D> lc;
+    make_lane_const<D>(lc, lane, wave, lds_addr(ring));
     const int64_t kv_stride = (int64_t)p.n_heads_kv * D;
     const uint16_t* kbase = p.k + (int64_t)s0 * kv_stride + (int64_t)g * D;
     const uint16_t* vbase = p.v + (int64_t)s0 * kv_stride + (int64_t)g * D;
-    int dma_r[LPW], dma_ck[LPW], dma_cv[LPW];
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-        const int byte = (wave * LPW + i) * 1024 + lane * 16;
-        dma_r[i] = byte / ROWB;
-        const int pos = (byte % ROWB) / 16;
-        dma_ck[i] = (pos ^ (dma_r[i] % CPR)) * 8;
-        dma_cv[i] = (pos ^ (2 * (dma_r[i] & 3))) * 8;
-    }
-    auto issue_tile = [&](int t, auto stage_c) {
-        constexpr int stage = decltype(stage_c)::value;
-        const int k0 = t * kKT;
-#pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            const int64_t row = (int64_t)min(k0 + dma_r[i], L - 1) * kv_stride;
-            char* kdst = lds + stage * STAGEB + (wave * LPW + i) * 1024;
-            __builtin_amdgcn_global_load_lds((glb_void*)(kbase + row + dma_ck[i]), (lds_void*)kdst, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glb_void*)(vbase + row + dma_cv[i]), (lds_void*)(kdst + TILEB), 16, 0, 0);
-        }
-    };
 
-    f32x16 o[NDB];
+    f32x16 o[G::NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < G::NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-    float m = -INFINITY, lsum = 0.f;            // running max in raw (unscaled) score units
+    float m = -INFINITY, lsum = 0.f;
 
-    // One tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-    auto compute = [&](int k0, auto stage_c, auto mask_c) {
-        constexpr int stage = decltype(stage_c)::value;
-        constexpr bool MASK = decltype(mask_c)::value;
-        const char* kt = lds + stage * STAGEB;
-        f32x16 sacc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const u32x4 a = *(const u32x4*)(kt + koff[ks]);
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[ks]), sacc, 0, 0, 0);
-        }
-        u32x2 vop[2][NDB][2];                   // V^T operands, read while the softmax runs
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                vop[j][db][0] = lds_read_tr16<stage * STAGEB>(voff[j][db][0]);
-                vop[j][db][1] = lds_read_tr16<stage * STAGEB>(voff[j][db][1]);
-            }
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (MASK && k0 + 8 * (i >> 2) + 4 * hf + (i & 3) > qrow) sacc[i] = -INFINITY;
-            tmax = fmaxf(tmax, sacc[i]);
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float mnew = fmaxf(m, tmax);      // finite: key 0 is in tile 0 for every row
-        if (__ballot(mnew > m) != 0) {          // rescale only when some running max moved
-            const float alpha = fast_exp2((m - mnew) * c);
-            lsum *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-            m = mnew;
-        }
-        const float mc = m * c;
-        float psum = 0.f;
-        uint32_t pk[8];
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-            const float p0 = fast_exp2(fmaf(sacc[i], c, -mc)), p1 = fast_exp2(fmaf(sacc[i + 1], c, -mc));
-            psum += p0 + p1;
-            pk[i >> 1] = pack_bf16x2(p0, p1);
-        }
-        lsum += psum;
-        wait_lgkm0();                           // the transpose reads have landed
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const u32x4 pb = {pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]};
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const u32x4 a = {vop[j][db][0][0], vop[j][db][0][1], vop[j][db][1][0], vop[j][db][1][1]};
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pb), o[db], 0, 0, 0);
-            }
-        }
-    };
     auto tile = [&](int t, auto stage_c) {
         constexpr int stage = decltype(stage_c)::value;
-        wait_vmcnt<2 * LPW>();                  // this wave's loads of tile t have landed
+        wait_vmcnt<2 * G::LPW>();               // this wave's loads of tile t have landed
         __builtin_amdgcn_s_barrier();           // ... and every wave's; tile t-1 is consumed
-        issue_tile(t + 2, std::integral_constant<int, (stage + 2) % kStages>{});
+        issue_tile<D, (stage + 2) % kStages>(ring, lc, kbase, vbase, kv_stride, (t + 2) * kKT, L, wave);
         if (t > last_tile) return;              // whole tile above this wave's diagonal
         const int k0 = t * kKT;
         if (k0 + kKT - 1 > wrow0)
-            compute(k0, stage_c, std::true_type{});
+            attend_tile<D, stage, true>(ring, lc, qreg, k0, qrow, hf, c, m, lsum, o);
         else
-            compute(k0, stage_c, std::false_type{});
+            attend_tile<D, stage, false>(ring, lc, qreg, k0, qrow, hf, c, m, lsum, o);
     };
-
-    issue_tile(0, std::integral_constant<int, 0>{});
-    issue_tile(1, std::integral_constant<int, 1>{});   // past the last tile it re-reads valid rows
+    issue_tile<D, 0>(ring, lc, kbase, vbase, kv_stride, 0, L, wave);
+    issue_tile<D, 1>(ring, lc, kbase, vbase, kv_stride, kKT, L, wave);   // past the end it re-reads valid rows
     for (int t = 0; t < ntiles; t += kStages) {
         tile(t, std::integral_constant<int, 0>{});
         if (t + 1 >= ntiles) break;
@@ -253,51 +391,445 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(const PrefillParam
         if (t + 2 >= ntiles) break;
         tile(t + 2, std::integral_constant<int, 2>{});
     }
-
     wait_vmcnt<0>();                            // the tiles issued past the end must land
     lsum += __shfl_xor(lsum, 32);
     const float inv = 1.f / lsum;
 
-    // Epilogue through LDS: each wave writes its 32 x D block (row-major,
-    // rows padded by 16 bytes) into the freed ring, then reads it back so
-    // that every store instruction writes whole contiguous row segments.
-    // Done in passes of 64 columns so the four waves fit the ring.
-    constexpr int OB = OUT_BF16 ? 2 : 4;        // output bytes per element
-    constexpr int PCOLS = D == 64 ? 32 : 64;    // columns per pass
-    constexpr int PROWB = PCOLS * OB + 16;      // padded LDS row bytes
-    constexpr int WAVEB = 32 * PROWB;           // LDS bytes per wave per pass
-    static_assert(4 * WAVEB <= kStages * STAGEB, "epilogue staging must fit the ring");
-    constexpr int CH = PCOLS * OB / 16;         // 16-byte chunks per row segment
     __builtin_amdgcn_s_barrier();               // every wave is done with the ring
-    char* wbuf = lds + wave * WAVEB;
+    const uint32_t wbuf = lds_addr(ring) + wave * E::WAVEB;
     const int64_t orow0 = (int64_t)(s0 + wrow0) * p.n_heads_q + h;   // output row of this wave's row 0
 #pragma unroll
-    for (int pass = 0; pass < D / PCOLS; ++pass) {
+    for (int pass = 0; pass < E::NPASS; ++pass) {
+        epi_stage<D, OUT_BF16>(wbuf, o, inv, pass, n, hf);
+        wait_lgkm0();
 #pragma unroll
-        for (int dbp = 0; dbp < PCOLS / 32; ++dbp) {
-            const int db = pass * (PCOLS / 32) + dbp;
+        for (int k = 0; k < E::SPP; ++k) {
+            const int chunk = k * 64 + lane;
+            const int row = chunk / E::CH, c16 = chunk % E::CH;
+            const u32x4 v = lds_read16(wbuf + row * E::PROWB + c16 * 16);
+            wait_lgkm0();
+            if (wrow0 + row < L)
+                *(u32x4*)((char*)p.out + ((orow0 + (int64_t)row * p.n_heads_q) * D + pass * E::PCOLS) * E::OB +
+                          c16 * 16) = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Plan: the non-empty work items of the pack, per XCD.  Unit u (sequence b =
+// u / per_seq, head block u % per_seq) belongs to XCD u % 8; an item is one
+// query tile of a unit.  Each XCD's list holds its units in order, each unit's
+// query tiles heaviest first, so that consecutive items share K/V.  One
+// workgroup; wave x builds XCD x's list (a count pass, then a scan pass).
+constexpr int kPlanThreads = kNumXcd * kWave;
+
+__device__ __forceinline__ int plan_unit_tiles(const PrefillParams& p, int u, int per_seq, int qt_rows, int& s0,
+                                               int& L) {
+    s0 = 0;
+    L = 0;
+    if (u >= p.n_units) return 0;
+    const int b = u / per_seq;
+    const int a = p.cu[b], e = p.cu[b + 1];
+    if (a < 0 || e < a || e > p.total_tokens || e - a > p.max_seqlen) {
+        raise_error(p.err, kErrCuSeqlens);
+        return 0;
+    }
+    s0 = a;
+    L = e - a;
+    return (L + qt_rows - 1) / qt_rows;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const PrefillParams p) {
+    __shared__ int tot[kNumXcd];
+    const int lane = threadIdx.x & 63, x = threadIdx.x >> 6;
+    const int per_seq = p.n_heads_kv * p.head_blocks;
+    const int qt_rows = 128 / p.heads_per_block;
+    const int n_mine = (p.n_units - x + kNumXcd - 1) / kNumXcd;   // units x, x + 8, ...
+    int total = 0;
+    for (int i = lane; i < n_mine; i += kWave) {
+        int s0, L;
+        total += plan_unit_tiles(p, i * kNumXcd + x, per_seq, qt_rows, s0, L);
+    }
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const int col = dbp * 32 + 8 * i4 + 4 * hf;
-                const float r0 = o[db][4 * i4] * inv, r1 = o[db][4 * i4 + 1] * inv;
-                const float r2 = o[db][4 * i4 + 2] * inv, r3 = o[db][4 * i4 + 3] * inv;
-                if constexpr (OUT_BF16)
-                    *(u32x2*)(wbuf + n * PROWB + col * OB) = u32x2{pack_bf16x2(r0, r1), pack_bf16x2(r2, r3)};
-                else
-                    *(f32x4*)(wbuf + n * PROWB + col * OB) = f32x4{r0, r1, r2, r3};
+    for (int o = 32; o > 0; o >>= 1) total += __shfl_xor(total, o);
+    if (lane == 0) tot[x] = total;
+    __syncthreads();
+    int pos0 = 0;
+    for (int y = 0; y < x; ++y) pos0 += tot[y];
+    if (lane == 0) {
+        p.plan_count[x] = total;
+        p.plan_off[x] = pos0;
+        p.plan_claim[x] = 0;
+    }
+    for (int base = 0; base < n_mine; base += kWave) {
+        const int i = base + lane;
+        int s0 = 0, L = 0;
+        const int nq = i < n_mine ? plan_unit_tiles(p, i * kNumXcd + x, per_seq, qt_rows, s0, L) : 0;
+        int incl = nq;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        int pos = pos0 + incl - nq;
+        const int unit_in_seq = (i * kNumXcd + x) % per_seq;
+        for (int j = 0; j < nq; ++j, ++pos) {
+            if (pos >= p.plan_cap) {
+                raise_error(p.err, kErrCuSeqlens);
+                break;
+            }
+            p.plan_items[pos] = int4{s0, L, unit_in_seq, nq - 1 - j};
+        }
+        pos0 += __shfl(incl, 63);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent workgroups over the plan.  The resident workgroups of an XCD take
+// that XCD's items in list order: workgroup l starts with item l, and each
+// later item comes from the XCD's counter (item index = workgroups per XCD +
+// ticket).  Claiming in order, each item shortly before it is needed, keeps
+// the items in flight a compact window of the list, so a unit's query tiles
+// run side by side and its K/V is read from HBM about once and from the XCD's
+// L2 after that.
+//
+// Vector-memory instructions are counted so that each tile's wait covers that
+// tile and nothing newer: per tile 2*LPW direct loads, at the end of an item
+// NST unconditional buffer stores and NKS Q loads for the next item (inline
+// asm).  Wave 0 also issues one counter atomic per item; it is left out of
+// the counts, which can only make a wait cover one more operation.
+//
+// A ticket reaches the other waves through LDS.  The ticket for the next item
+// is claimed when two tiles of the current one are left to load, just before
+// a tile's loads; two steps later the wait for that tile has covered it, and
+// wave 0 writes it to LDS before that step's barrier.  The issue side reads it
+// when it starts the next item, which is exactly then.  Only items of a single
+// tile need it sooner: wave 0 then waits for all its memory operations and the
+// workgroup takes one extra barrier.
+// One counter increment by lane `sel` (0 or 1) of the wave; the old value
+// lands in that lane of tk, written in place (tk is an in/out operand, so the
+// register is never copied while the atomic is in flight).
+__device__ __forceinline__ void claim_ticket(uint32_t& tk, int sel, int* counter) {
+    uint64_t saved;
+    const uint64_t lane_mask = 1ull << sel;
+    asm volatile(
+        "s_mov_b64 %1, exec\n\t"
+        "s_and_b64 exec, exec, %4\n\t"
+        "global_atomic_add %0, %2, %3, %5 sc0\n\t"
+        "s_mov_b64 exec, %1"
+        : "+v"(tk), "=&s"(saved)
+        : "v"(0u), "v"(1u), "s"(lane_mask), "s"(counter)
+        : "memory");
+}
+// Lane `sel` of v (uniform result).
+__device__ __forceinline__ uint32_t read_lane(uint32_t v, int sel) {
+    uint32_t r;
+    asm volatile("v_readlane_b32 %0, %1, %2" : "=s"(r) : "v"(v), "s"(sel));
+    return r;
+}
+// A uniform value the optimiser cannot see through: selects between such
+// values stay selects of values (a select between two loads of one object
+// is otherwise folded into one load at a computed offset, which keeps that
+// object in private memory).
+__device__ __forceinline__ int opaque_uniform(int v) {
+    asm volatile("" : "+s"(v));
+    return v;
+}
+__device__ __forceinline__ uint32_t read_lane0(uint32_t v) {
+    uint32_t r;
+    asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(r) : "v"(v));
+    return r;
+}
+__device__ __forceinline__ void lds_write4_wait(uint32_t addr, uint32_t v) {
+    asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ int lds_read4_uniform(uint32_t addr) {
+    uint32_t r;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(addr) : "memory");
+    return (int)read_lane0(r);
+}
+
+// Work item as read from the plan.
+struct PItem {
+    int s0, L, q0, ntiles, g, h0;               // h0: first query head of the item
+};
+
+// State of one persistent workgroup.  Everything lives in this one object,
+// reached only through its members, so that after inlining every field is
+// promoted to a register (state shared by nested closures can stay in
+// private memory).
+template <int D, int NH, bool OUT_BF16>
+struct PersistentTask {
+    using G = Geo<D>;
+    using E = Epi<D, OUT_BF16>;
+    static constexpr int QT = 128 / NH;
+    static constexpr int WPH = 4 / NH;
+    static constexpr int DMA = 2 * G::LPW;      // vector-memory ops per tile issue
+    static constexpr int QL = G::NKS;           // Q loads per item
+    static constexpr int ST = E::NST;           // output stores per item
+
+    // fixed
+    const PrefillParams* pp;
+    char* ring;
+    const int4* list;
+    int* counter;
+    int cnt, wx, lane, wave, n, hf;
+    float c;
+    int64_t kv_stride, out_bytes;
+    uint32_t wbuf, slot_addr;
+    LaneConst<D> lc;
+    // ticket of the next item (lane 0 of wave 0) and the LDS slot it is published in
+    uint32_t tk;
+    int slot_item, slot_pub;                    // item the slot holds, step whose barrier published it
+    bool pend;                                  // a claimed ticket is not yet published
+    int pend_item, pend_ps;                     // its item and the step from which it has landed
+    // issue side: two tiles ahead of the compute side
+    PItem iu;
+    int ki, ti;                                 // item number and next tile within it
+    bool claimed;                               // the ticket of item ki + 1 is claimed
+    bool need_next;                             // iu is fully issued: start item ki + 1 at the next call
+    bool idone;                                 // no item after iu
+    int ih0, ih1;                               // list index of items ki, ki - 1
+    // compute side
+    PItem cu;
+    int jc, tc, h, wrow0, qrow, last_tile;
+    u32x4 qreg[G::NKS];
+    f32x16 o[G::NDB];
+    float m, lsum;
+    int end1, end2;                             // what the two previous steps issued at their end: 0 nothing,
+                                                // 1 a store burst (ST ops), 2 stores then Q loads (ST + QL ops)
+    bool fresh, done;
+    int step_no;
+
+    __device__ __forceinline__ PItem decode(int idx) const {
+        const int4 e = scalar_load16(list + idx);
+        PItem u;
+        u.s0 = e.x;
+        u.L = e.y;
+        u.g = e.z / pp->head_blocks;
+        u.h0 = u.g * pp->group + (e.z % pp->head_blocks) * NH;
+        u.q0 = e.w * QT;
+        u.ntiles = (min(u.q0 + QT, u.L) + kKT - 1) / kKT;
+        return u;
+    }
+
+    __device__ __forceinline__ void publish(int step) {
+        if (wave == 0) lds_write4_wait(slot_addr, (uint32_t)wx + read_lane(tk, 0));
+        slot_item = pend_item;
+        slot_pub = step;
+        pend = false;
+    }
+
+    template <int STAGE>
+    __device__ __forceinline__ void issue_next(int step) {
+        if (need_next) {                        // start item ki + 1
+            need_next = false;
+            const int want = ki + 1;
+            const bool ready = opaque_uniform(slot_item) == want && opaque_uniform(slot_pub) <= step;
+            if (!ready) {                       // single-tile item: wait for the ticket explicitly
+                if (wave == 0) wait_vmcnt<0>();
+                if (pend) publish(step);
+                __builtin_amdgcn_s_barrier();
+            }
+            const int idx = lds_read4_uniform(slot_addr);
+            ki = want;
+            ih1 = ih0;
+            ih0 = idx;
+            if (idx < cnt) {
+                iu = decode(idx);
+                ti = 0;
+                claimed = false;
+            } else {
+                idone = true;
             }
         }
-        __builtin_amdgcn_wave_barrier();        // the wave reads back what its lanes wrote
-#pragma unroll
-        for (int k = 0; k < 32 * CH / 64; ++k) {
-            const int chunk = k * 64 + lane;
-            const int row = chunk / CH, c16 = chunk % CH;
-            const u32x4 v = *(const u32x4*)(wbuf + row * PROWB + c16 * 16);
-            if (wrow0 + row < L)
-                *(u32x4*)((char*)p.out + ((orow0 + (int64_t)row * p.n_heads_q) * D + pass * PCOLS) * OB + c16 * 16) = v;
+        if (!idone && !claimed && iu.ntiles - ti <= 2) {   // ticket of item ki + 1, before this call's loads
+            if (wave == 0) claim_ticket(tk, 0, counter);
+            claimed = true;
+            pend = true;
+            pend_item = ki + 1;
+            pend_ps = step + 2;
         }
-        __builtin_amdgcn_wave_barrier();        // before the next pass overwrites the buffer
+        const uint16_t* kb = pp->k + (int64_t)iu.s0 * kv_stride + (int64_t)iu.g * D;
+        const uint16_t* vb = pp->v + (int64_t)iu.s0 * kv_stride + (int64_t)iu.g * D;
+        const int t = idone ? iu.ntiles - 1 : ti;   // past the last item: re-read its last tile
+        issue_tile<D, STAGE>(ring, lc, kb, vb, kv_stride, t * kKT, iu.L, wave);
+        if (!idone && ++ti == iu.ntiles) need_next = true;
     }
+
+    __device__ __forceinline__ void bind() {
+        h = cu.h0 + wave / WPH;
+        wrow0 = cu.q0 + (wave % WPH) * 32;
+        qrow = wrow0 + n;
+        last_tile = wrow0 < cu.L ? min(wrow0 + 31, cu.L - 1) / kKT : -1;
+    }
+    __device__ __forceinline__ void load_q() {
+        const uint16_t* qp = pp->q + ((int64_t)(cu.s0 + min(qrow, cu.L - 1)) * pp->n_heads_q + h) * D + hf * 8;
+#pragma unroll
+        for (int ks = 0; ks < G::NKS; ++ks) qreg[ks] = global_load16(qp + ks * 16);
+    }
+    __device__ __forceinline__ void reset() {
+#pragma unroll
+        for (int db = 0; db < G::NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+        m = -INFINITY;
+        lsum = 0.f;
+    }
+
+    // The finished item's output: rows u.s0 + u.q0 .. +QT of heads u.h0 ..
+    // +NH, stored with buffer stores (offsets of rows outside the sequence are
+    // out of range, so those stores are dropped and the count is fixed).
+    __device__ __forceinline__ void epilogue(const PItem& u, int u_wrow0, int u_h) {
+        const float inv = 1.f / (lsum + __shfl_xor(lsum, 32));
+        const int64_t base = ((int64_t)(u.s0 + u.q0) * pp->n_heads_q) * D * E::OB;
+        const int64_t span = min((int64_t)QT * pp->n_heads_q * D * E::OB, out_bytes - base);
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((char*)pp->out + base, 0, (int)span, 0x00020000);
+#pragma unroll
+        for (int pass = 0; pass < E::NPASS; ++pass) {
+            epi_stage<D, OUT_BF16>(wbuf, o, inv, pass, n, hf);
+            wait_lgkm0();
+#pragma unroll
+            for (int k = 0; k < E::SPP; ++k) {
+                const int chunk = k * 64 + lane;
+                const int row = chunk / E::CH, c16 = chunk % E::CH;
+                const u32x4 v = lds_read16(wbuf + row * E::PROWB + c16 * 16);
+                const int r = u_wrow0 - u.q0 + row;
+                const int off = u_wrow0 + row < u.L
+                                    ? (int)(((int64_t)r * pp->n_heads_q + u_h) * D * E::OB +
+                                            pass * E::PCOLS * E::OB + c16 * 16)
+                                    : 0x7FFFFFF0;
+                wait_lgkm0();
+                __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, off, 0, 0);
+            }
+        }
+    }
+
+    template <int STAGE>
+    __device__ __forceinline__ void step() {
+        // wait for this tile's loads: everything issued after them may stay in flight
+        const int nst = (end1 != 0) + (end2 != 0), nql = (end1 == 2) + (end2 == 2);
+        if (nst == 0)
+            wait_vmcnt<DMA>();
+        else if (nst == 1)
+            nql == 0 ? wait_vmcnt<DMA + ST>() : wait_vmcnt<DMA + QL + ST>();
+        else if (nql == 0)
+            wait_vmcnt<DMA + 2 * ST>();
+        else
+            nql == 1 ? wait_vmcnt<DMA + QL + 2 * ST>() : wait_vmcnt<DMA + 2 * QL + 2 * ST>();
+        if (pend && pend_ps <= step_no) publish(step_no);   // the ticket has landed
+        __builtin_amdgcn_s_barrier();           // every wave's loads landed; the previous tile is consumed
+        issue_next<(STAGE + 2) % kStages>(step_no);
+        if (fresh) wait_vmcnt<DMA>();           // this item's Q rows (issued just before this step's tile loads)
+#pragma unroll
+        for (int ks = 0; ks < G::NKS; ++ks) pin_after_wait(qreg[ks]);
+        const int k0 = tc * kKT;
+        if (tc <= last_tile) {
+            // one body for both cases (two inlined copies would double the live registers)
+            attend_tile<D, STAGE, true>(ring, lc, qreg, k0, qrow, hf, c, m, lsum, o, k0 + kKT - 1 > wrow0);
+        }
+        end2 = end1;
+        end1 = 0;
+        fresh = false;
+        ++step_no;
+        if (++tc == cu.ntiles) {
+            // the issue side has started item jc + 1 and at most one more
+            const int a0 = opaque_uniform(ih0), a1 = opaque_uniform(ih1);
+            const int nidx = ki == jc + 1 ? a0 : a1;
+            const bool more = nidx >= 0 && nidx < cnt;
+            const PItem fin = cu;
+            const int fin_wrow0 = wrow0, fin_h = h;
+            if (more) {
+                cu = decode(nidx);
+                bind();
+            }
+            epilogue(fin, fin_wrow0, fin_h);    // ST ops
+            if (more) load_q();                 // QL ops, after the stores: qreg is free during the epilogue
+            end1 = more ? 2 : 1;
+            reset();
+            ++jc;
+            tc = 0;
+            fresh = more;
+            done = !more;
+        }
+    }
+};
+
+template <int D, int NH, bool OUT_BF16>
+__global__ __launch_bounds__(256, 2) void prefill_persistent_kernel(const PrefillParams p) {
+    using G = Geo<D>;
+    using E = Epi<D, OUT_BF16>;
+    __shared__ __attribute__((aligned(1024))) char ring[kStages * G::STAGEB + 4 * E::WAVEB];
+    __shared__ int slot[1];                     // list index of the next item
+
+    const int x = blockIdx.x % kNumXcd, l = blockIdx.x / kNumXcd;
+    const int cnt = scalar_load4(p.plan_count + x);
+    if (l >= cnt) return;
+
+    PersistentTask<D, NH, OUT_BF16> T;
+    T.pp = &p;
+    T.ring = ring;
+    T.list = p.plan_items + scalar_load4(p.plan_off + x);
+    T.counter = p.plan_claim + x;
+    T.cnt = cnt;
+    T.wx = gridDim.x / kNumXcd;
+    T.lane = threadIdx.x & 63;
+    T.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: wave-0 work is a scalar branch
+    T.n = T.lane & 31;
+    T.hf = T.lane >> 5;
+    T.c = p.scale_log2;
+    T.kv_stride = (int64_t)p.n_heads_kv * D;
+    T.out_bytes = (int64_t)p.total_tokens * p.n_heads_q * D * E::OB;
+    T.wbuf = lds_addr(ring) + kStages * G::STAGEB + T.wave * E::WAVEB;
+    T.slot_addr = lds_addr(slot);
+    make_lane_const<D>(T.lc, T.lane, T.wave, lds_addr(ring));
+
+    // ticket of item 1, claimed up front
+    T.tk = 0;
+    if (T.wave == 0) {
+        claim_ticket(T.tk, 0, T.counter);
+        wait_vmcnt<0>();
+        lds_write4_wait(T.slot_addr, (uint32_t)T.wx + read_lane(T.tk, 0));
+    }
+    __builtin_amdgcn_s_barrier();
+    T.slot_item = 1;
+    T.slot_pub = -1000;
+    T.pend = false;
+    T.pend_item = 0;
+    T.pend_ps = 0;
+
+    T.iu = T.decode(l);
+    T.ki = 0;
+    T.ti = 0;
+    T.claimed = true;
+    T.need_next = false;
+    T.idone = false;
+    T.ih0 = l;
+    T.ih1 = -1;
+    T.cu = T.iu;
+    T.jc = 0;
+    T.tc = 0;
+    T.bind();
+    T.reset();
+    T.end1 = 0;
+    T.end2 = 0;
+    T.fresh = false;
+    T.done = false;
+    T.step_no = 0;
+
+    T.load_q();
+    T.template issue_next<0>(-2);
+    T.template issue_next<1>(-1);
+    for (;;) {
+        T.template step<0>();
+        if (T.done) break;
+        T.template step<1>();
+        if (T.done) break;
+        T.template step<2>();
+        if (T.done) break;
+    }
+    wait_vmcnt<0>();                            // loads and tickets issued past the end land before the LDS is released
 }
 
 template <int D, int NH, bool OUT_BF16>
@@ -311,17 +843,45 @@ hipError_t launch_variant(const PrefillParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int D, int NH, bool OUT_BF16>
+hipError_t launch_persistent(const PrefillParams& p, int num_cus, hipStream_t stream) {
+    static int per_cu = 0;                      // resident workgroups per CU (one device type)
+    if (per_cu == 0) {
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, (const void*)prefill_persistent_kernel<D, NH, OUT_BF16>, 256, 0);
+        if (e != hipSuccess || per_cu <= 0) per_cu = 1;
+    }
+    const int grid = max(kNumXcd, per_cu * num_cus / kNumXcd * kNumXcd);
+    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((prefill_persistent_kernel<D, NH, OUT_BF16>), dim3(grid), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D, int NH, bool OUT_BF16>
+hipError_t dispatch(const PrefillParams& p, bool persistent, int num_cus, hipStream_t stream) {
+    return persistent ? launch_persistent<D, NH, OUT_BF16>(p, num_cus, stream)
+                      : launch_variant<D, NH, OUT_BF16>(p, stream);
+}
+
 }  // namespace
 
-hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, bool out_bf16,
+hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, bool out_bf16, bool persistent, int num_cus,
                                hipStream_t stream) {
     const int nh = p.heads_per_block;
     if (head_dim == 128) {
-        if (nh == 2) return out_bf16 ? launch_variant<128, 2, true>(p, stream) : launch_variant<128, 2, false>(p, stream);
-        return out_bf16 ? launch_variant<128, 1, true>(p, stream) : launch_variant<128, 1, false>(p, stream);
+        if (nh == 2)
+            return out_bf16 ? dispatch<128, 2, true>(p, persistent, num_cus, stream)
+                            : dispatch<128, 2, false>(p, persistent, num_cus, stream);
+        return out_bf16 ? dispatch<128, 1, true>(p, persistent, num_cus, stream)
+                        : dispatch<128, 1, false>(p, persistent, num_cus, stream);
     }
-    if (nh == 2) return out_bf16 ? launch_variant<64, 2, true>(p, stream) : launch_variant<64, 2, false>(p, stream);
-    return out_bf16 ? launch_variant<64, 1, true>(p, stream) : launch_variant<64, 1, false>(p, stream);
+    if (nh == 2)
+        return out_bf16 ? dispatch<64, 2, true>(p, persistent, num_cus, stream)
+                        : dispatch<64, 2, false>(p, persistent, num_cus, stream);
+    return out_bf16 ? dispatch<64, 1, true>(p, persistent, num_cus, stream)
+                    : dispatch<64, 1, false>(p, persistent, num_cus, stream);
 }
 
 }  // namespace slm

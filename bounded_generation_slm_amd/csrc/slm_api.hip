@@ -28,6 +28,9 @@ struct slm_ctx {
     size_t topk_ws_bytes = 0;
     int64_t topk_lists = 0;         // stage-1 lists (of up to max_beams keys) per request
     int* err_flag = nullptr;
+    int4* plan_items = nullptr;     // prefill work list: [plan_cap] entries, then 3 x 8 ints
+    int plan_cap = 0;
+    int num_cus = 256;
     size_t max_lds = 0;
     char last_error[512] = {0};
 };
@@ -108,6 +111,9 @@ slm_status slm_ctx_create(int device, const slm_caps* caps, slm_ctx** out) {
         if (c.max_requests <= 0) c.max_requests = 64;
         if (c.max_beams <= 0) c.max_beams = slm::kTopkMaxWidth;
         if (c.max_vocab <= 0) c.max_vocab = 262144;
+        if (c.max_tokens <= 0) c.max_tokens = 1 << 20;
+        if (c.max_seqs <= 0) c.max_seqs = 8192;
+        if (c.max_heads_q <= 0) c.max_heads_q = 64;
         ctx->caps = c;
         ctx->max_lds = 160 * 1024;          // gfx950 LDS per workgroup
         *out = ctx;
@@ -122,6 +128,9 @@ slm_status slm_ctx_create(int device, const slm_caps* caps, slm_ctx** out) {
     if (c.max_requests <= 0) c.max_requests = 64;
     if (c.max_beams <= 0) c.max_beams = slm::kTopkMaxWidth;
     if (c.max_vocab <= 0) c.max_vocab = 262144;
+    if (c.max_tokens <= 0) c.max_tokens = 1 << 20;
+    if (c.max_seqs <= 0) c.max_seqs = 8192;
+    if (c.max_heads_q <= 0) c.max_heads_q = 64;
     ctx->caps = c;
     if (hipSetDevice(device) != hipSuccess) {
         delete ctx;
@@ -133,15 +142,24 @@ slm_status slm_ctx_create(int device, const slm_caps* caps, slm_ctx** out) {
         return SLM_ERR_DEVICE;
     }
     ctx->max_lds = prop.sharedMemPerBlock;
+    ctx->num_cus = prop.multiProcessorCount;
+    const int64_t entries = slm::prefill_plan_entries(c.max_tokens, c.max_seqs, c.max_heads_q);
+    if (entries > INT32_MAX - 16) {
+        delete ctx;
+        return SLM_ERR_INVALID_ARG;
+    }
+    ctx->plan_cap = (int)entries;
     ctx->topk_ws_bytes = slm::beam_topk_workspace_bytes(c.max_requests, c.max_beams);
     ctx->topk_lists = std::max<int64_t>((int64_t)c.max_beams, slm::kTopkMaxChunks);
     if (hipMalloc((void**)&ctx->topk_ws, ctx->topk_ws_bytes) != hipSuccess ||
         hipMemset(ctx->topk_ws, 0, ctx->topk_ws_bytes) != hipSuccess ||
         hipMalloc((void**)&ctx->err_flag, sizeof(int)) != hipSuccess ||
         hipMemset(ctx->err_flag, 0, sizeof(int)) != hipSuccess ||
+        hipMalloc((void**)&ctx->plan_items, sizeof(int4) * ((size_t)ctx->plan_cap + 8)) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {
         if (ctx->topk_ws) (void)hipFree(ctx->topk_ws);
         if (ctx->err_flag) (void)hipFree(ctx->err_flag);
+        if (ctx->plan_items) (void)hipFree(ctx->plan_items);
         delete ctx;
         return SLM_ERR_OOM;
     }
@@ -155,6 +173,7 @@ void slm_ctx_destroy(slm_ctx* ctx) {
         (void)hipDeviceSynchronize();
         (void)hipFree(ctx->topk_ws);
         (void)hipFree(ctx->err_flag);
+        (void)hipFree(ctx->plan_items);
     }
     delete ctx;
 }
@@ -206,6 +225,9 @@ slm_status slm_packed_prefill_attn(slm_ctx* ctx, const uint16_t* q, const uint16
         return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: tensors must be 16-byte aligned");
     if (max_seqlen > total_tokens)
         return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: max_seqlen %d > total_tokens %d", max_seqlen, total_tokens);
+    if (total_tokens > ctx->caps.max_tokens || num_seqs > ctx->caps.max_seqs || n_heads_q > ctx->caps.max_heads_q)
+        return fail(ctx, SLM_ERR_CAPACITY, "prefill: beyond the context caps (tokens %d, seqs %d, heads %d)",
+                    ctx->caps.max_tokens, ctx->caps.max_seqs, ctx->caps.max_heads_q);
     const size_t T = (size_t)total_tokens, D = (size_t)head_dim;
     const size_t qb = T * n_heads_q * D * 2, kb = T * n_heads_kv * D * 2;
     const size_t ob = T * n_heads_q * D * (out_dtype == SLM_F32 ? 4 : 2);
@@ -225,7 +247,17 @@ slm_status slm_packed_prefill_attn(slm_ctx* ctx, const uint16_t* q, const uint16
     if (units > INT32_MAX / 8) return fail(ctx, SLM_ERR_UNSUPPORTED, "prefill: too many sequences x heads");
     p.n_units = (int)units;
     p.scale_log2 = scale * 1.4426950408889634f;
-    return SLM_LAUNCH(ctx, slm::launch_prefill_attn(p, head_dim, out_dtype == SLM_BF16, ctx->stream), "prefill");
+    p.plan_items = ctx->plan_items;
+    p.plan_cap = ctx->plan_cap;
+    p.plan_count = (int*)(ctx->plan_items + ctx->plan_cap);
+    p.plan_off = p.plan_count + 8;
+    p.plan_claim = p.plan_off + 8;
+    // Large packs run as persistent workgroups over a device-built work list;
+    // small ones launch one workgroup per work unit (no planning launch).
+    const int64_t est_units = ((int64_t)total_tokens * n_heads_q / 128) + 1;
+    const bool persistent = est_units >= 8LL * ctx->num_cus;
+    return SLM_LAUNCH(ctx, slm::launch_prefill_attn(p, head_dim, out_dtype == SLM_BF16, persistent, ctx->num_cus,
+                                                    ctx->stream), "prefill");
 }
 
 slm_status slm_gather_last(slm_ctx* ctx, const void* hidden, const int32_t* cu_seqlens, int32_t num_seqs,

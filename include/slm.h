@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SLM_ABI_VERSION 1
+#define SLM_ABI_VERSION 2
 
 typedef enum {
     SLM_OK = 0,
@@ -63,11 +63,16 @@ typedef struct {
     int32_t max_requests;   /* requests per beam call                 (64)      */
     int32_t max_beams;      /* beam width and beams in                (512)     */
     int32_t max_vocab;      /* vocabulary size                        (262144)  */
+    int32_t max_tokens;     /* packed prefill tokens per call         (1048576) */
+    int32_t max_seqs;       /* packed prefill sequences per call      (8192)    */
+    int32_t max_heads_q;    /* prefill query heads                    (64)      */
 } slm_caps;
 
 /* Create a context on HIP device `device`: sets that device current,
  * allocates the top-k workspace (about max_requests * max_beams^2 * 8 bytes)
- * and uses the null stream until slm_ctx_set_stream.  *out is NULL on error.
+ * and the prefill work-list workspace (about 16 * max_heads_q *
+ * (max_tokens / 128 + max_seqs) bytes), and uses the null stream until
+ * slm_ctx_set_stream.  *out is NULL on error.
  * device < 0 creates a dry-run context: every call performs its host-side
  * validation and returns its status without touching any device (usable on
  * machines without a GPU, e.g. to check argument handling). */
@@ -95,7 +100,8 @@ int slm_abi_version(void);
  * (causal, diagonal included, no attention across sequences); query head h
  * reads KV head h / (Hq/Hkv).  Supported: head_dim 64 or 128, Hq % Hkv == 0.
  * Empty sequences are allowed and produce no rows.  out must not overlap
- * q, k, v or cu_seqlens.
+ * q, k, v or cu_seqlens.  total_tokens, num_seqs and n_heads_q must be within
+ * the context caps (SLM_ERR_CAPACITY).
  */
 slm_status slm_packed_prefill_attn(slm_ctx *ctx, const uint16_t *q, const uint16_t *k,
                                    const uint16_t *v, const int32_t *cu_seqlens,

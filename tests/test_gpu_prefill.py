@@ -103,6 +103,27 @@ def test_throughput_workload_sampled_rows(gpu):
     assert_attn_close(got, ref, "prefill_throughput sampled")
 
 
+@pytest.mark.parametrize("Hq,Hkv,D", [(16, 8, 128), (16, 4, 64)])
+def test_persistent_many_short_sequences(gpu, Hq, Hkv, D):
+    """A pack large enough for the persistent form (at least eight 128-row work
+    units per CU) made mostly of short sequences: single-tile items (whose next
+    item is needed before a freshly claimed index is known to have landed),
+    empty sequences and a few long ones.  Every row against the oracle, and two
+    launches bitwise equal."""
+    rng = np.random.default_rng(11)
+    lengths = rng.integers(0, 49, 1600)
+    lengths[::97] = 300
+    shape = wl.PrefillShape("short_pack", 78, tuple(int(v) for v in lengths), Hq, Hkv, D)
+    assert shape.total_tokens * Hq // 128 + 1 >= 8 * 256
+    note("prefill persistent short pack T=%d Hq=%d Hkv=%d D=%d" % (shape.total_tokens, Hq, Hkv, D))
+    x = wl.prefill_inputs(shape)
+    out = _run(gpu, x, Hq, Hkv, D)
+    out2 = _run(gpu, x, Hq, Hkv, D)
+    assert torch.equal(out, out2)
+    ref = oracle.prefill_attn(x["q"], x["k"], x["v"], x["cu_seqlens"])
+    assert_attn_close(host_f64(out), ref, "short pack")
+
+
 def test_bad_cu_seqlens_is_flagged(gpu):
     note("prefill bad cu_seqlens -> device error flag")
     x = wl.prefill_inputs(wl.PrefillShape("bad", 5, (10, 10, 10), 4, 2, 64))
