@@ -287,7 +287,7 @@ def main():
             "value_counts": "prefill tokens per step (each through 28 layers) / whole-step time",
         },
         "roofline": {
-            "kernel": "prefill_attn_kernel<128,2,f32>",
+            "kernel": "prefill_persistent_kernel<128,2,f32> with its prefill_plan_kernel (one prefill call)",
             "bound": "hbm",
             "achieved": round(achieved_gbs, 1),
             "peak": HBM_PEAK_GBS,
@@ -295,7 +295,7 @@ def main():
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": pbytes,
-            "avg_launch_us": round(prefill_us, 2),
+            "avg_launch_us": round(prefill_us, 2),          # events around the call: plan + persistent kernel
             "mfma_tflops_causal": round(mfma_tflops, 1),
             "mfma_frac": round(mfma_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "mfma_frac_ceiling_at_hbm_peak": round(min(1.0, pflops / pbytes * HBM_PEAK_GBS * 1e9 / 1e12

@@ -37,6 +37,8 @@ struct PrefillParams {
 };
 hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, bool out_bf16, bool persistent,
                                int num_cus, hipStream_t stream);
+// the persistent form stages cu_seqlens in LDS: packs of fewer sequences only
+constexpr int kPrefillPlanMaxSeqs = 15999;
 // plan entries a pack can need: sum over sequences of ceil(L / qt_rows), per unit column
 inline int64_t prefill_plan_entries(int64_t max_tokens, int64_t max_seqs, int64_t max_heads_q) {
     return max_tokens * max_heads_q / 128 + max_seqs * max_heads_q;

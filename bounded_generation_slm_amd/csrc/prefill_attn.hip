@@ -419,17 +419,18 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(const PrefillParam
 // Plan: the non-empty work items of the pack, per XCD.  Unit u (sequence b =
 // u / per_seq, head block u % per_seq) belongs to XCD u % 8; an item is one
 // query tile of a unit.  Each XCD's list holds its units in order, each unit's
-// query tiles heaviest first, so that consecutive items share K/V.  One
-// workgroup; wave x builds XCD x's list (a count pass, then a scan pass).
-constexpr int kPlanThreads = kNumXcd * kWave;
+// query tiles heaviest first, so that consecutive items share K/V.  Workgroup
+// x builds XCD x's list: it stages cu_seqlens in LDS, counts the tiles of
+// every XCD's list (for the list offsets), then scans and writes its own units.
+constexpr int kPlanThreads = 256;
 
-__device__ __forceinline__ int plan_unit_tiles(const PrefillParams& p, int u, int per_seq, int qt_rows, int& s0,
-                                               int& L) {
+__device__ __forceinline__ int plan_unit_tiles(const PrefillParams& p, const int* cu, int u, int per_seq,
+                                               int qt_rows, int& s0, int& L) {
     s0 = 0;
     L = 0;
     if (u >= p.n_units) return 0;
     const int b = u / per_seq;
-    const int a = p.cu[b], e = p.cu[b + 1];
+    const int a = cu[b], e = cu[b + 1];
     if (a < 0 || e < a || e > p.total_tokens || e - a > p.max_seqlen) {
         raise_error(p.err, kErrCuSeqlens);
         return 0;
@@ -440,38 +441,65 @@ __device__ __forceinline__ int plan_unit_tiles(const PrefillParams& p, int u, in
 }
 
 __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const PrefillParams p) {
+    extern __shared__ int cu_lds[];             // cu_seqlens, num_seqs + 1 entries
     __shared__ int tot[kNumXcd];
-    const int lane = threadIdx.x & 63, x = threadIdx.x >> 6;
+    __shared__ int wsum[kPlanThreads / kWave];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, x = blockIdx.x;
+    for (int i = tid; i <= p.num_seqs; i += kPlanThreads) cu_lds[i] = p.cu[i];
+    if (tid < kNumXcd) tot[tid] = 0;
+    __syncthreads();
     const int per_seq = p.n_heads_kv * p.head_blocks;
     const int qt_rows = 128 / p.heads_per_block;
-    const int n_mine = (p.n_units - x + kNumXcd - 1) / kNumXcd;   // units x, x + 8, ...
-    int total = 0;
-    for (int i = lane; i < n_mine; i += kWave) {
+    // Sequence b's per_seq units u = b * per_seq + j have one tile count; unit
+    // j of it lands on XCD (b * per_seq + j) % 8.
+    int mine[kNumXcd];
+#pragma unroll
+    for (int y = 0; y < kNumXcd; ++y) mine[y] = 0;
+    for (int b = tid; b < p.num_seqs; b += kPlanThreads) {
         int s0, L;
-        total += plan_unit_tiles(p, i * kNumXcd + x, per_seq, qt_rows, s0, L);
+        const int nq = plan_unit_tiles(p, cu_lds, b * per_seq, per_seq, qt_rows, s0, L);
+        const int first = (b * per_seq) % kNumXcd;
+#pragma unroll
+        for (int y = 0; y < kNumXcd; ++y) {
+            const int j0 = (y - first + kNumXcd) % kNumXcd;      // first j of this sequence on XCD y
+            mine[y] += j0 < per_seq ? nq * ((per_seq - j0 + kNumXcd - 1) / kNumXcd) : 0;
+        }
     }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) total += __shfl_xor(total, o);
-    if (lane == 0) tot[x] = total;
+    for (int y = 0; y < kNumXcd; ++y) {
+        int v = mine[y];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+        if (lane == 0 && v) atomicAdd(&tot[y], v);
+    }
     __syncthreads();
     int pos0 = 0;
     for (int y = 0; y < x; ++y) pos0 += tot[y];
-    if (lane == 0) {
-        p.plan_count[x] = total;
+    if (tid == 0) {
+        p.plan_count[x] = tot[x];
         p.plan_off[x] = pos0;
         p.plan_claim[x] = 0;
     }
-    for (int base = 0; base < n_mine; base += kWave) {
-        const int i = base + lane;
+    const int n_mine = (p.n_units - x + kNumXcd - 1) / kNumXcd;   // units x, x + 8, ...
+    for (int base = 0; base < n_mine; base += kPlanThreads) {
+        const int i = base + tid;
         int s0 = 0, L = 0;
-        const int nq = i < n_mine ? plan_unit_tiles(p, i * kNumXcd + x, per_seq, qt_rows, s0, L) : 0;
+        const int nq = i < n_mine ? plan_unit_tiles(p, cu_lds, i * kNumXcd + x, per_seq, qt_rows, s0, L) : 0;
         int incl = nq;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const int y = __shfl_up(incl, o);
             if (lane >= o) incl += y;
         }
-        int pos = pos0 + incl - nq;
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        int before = 0, all = 0;
+#pragma unroll
+        for (int w = 0; w < kPlanThreads / kWave; ++w) {
+            before += w < wave ? wsum[w] : 0;
+            all += wsum[w];
+        }
+        int pos = pos0 + before + incl - nq;
         const int unit_in_seq = (i * kNumXcd + x) % per_seq;
         for (int j = 0; j < nq; ++j, ++pos) {
             if (pos >= p.plan_cap) {
@@ -480,7 +508,8 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const Prefil
             }
             p.plan_items[pos] = int4{s0, L, unit_in_seq, nq - 1 - j};
         }
-        pos0 += __shfl(incl, 63);
+        pos0 += all;
+        __syncthreads();                        // wsum is rewritten by the next chunk
     }
 }
 
@@ -852,7 +881,8 @@ hipError_t launch_persistent(const PrefillParams& p, int num_cus, hipStream_t st
         if (e != hipSuccess || per_cu <= 0) per_cu = 1;
     }
     const int grid = max(kNumXcd, per_cu * num_cus / kNumXcd * kNumXcd);
-    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
+    const size_t plan_lds = sizeof(int) * ((size_t)p.num_seqs + 1);   // num_seqs < kPrefillPlanMaxSeqs
+    hipLaunchKernelGGL(prefill_plan_kernel, dim3(kNumXcd), dim3(kPlanThreads), plan_lds, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill_persistent_kernel<D, NH, OUT_BF16>), dim3(grid), dim3(256), 0, stream, p);

@@ -255,7 +255,7 @@ slm_status slm_packed_prefill_attn(slm_ctx* ctx, const uint16_t* q, const uint16
     // Large packs run as persistent workgroups over a device-built work list;
     // small ones launch one workgroup per work unit (no planning launch).
     const int64_t est_units = ((int64_t)total_tokens * n_heads_q / 128) + 1;
-    const bool persistent = est_units >= 8LL * ctx->num_cus;
+    const bool persistent = est_units >= 8LL * ctx->num_cus && num_seqs <= slm::kPrefillPlanMaxSeqs;
     return SLM_LAUNCH(ctx, slm::launch_prefill_attn(p, head_dim, out_dtype == SLM_BF16, persistent, ctx->num_cus,
                                                     ctx->stream), "prefill");
 }

@@ -103,13 +103,13 @@ def test_throughput_workload_sampled_rows(gpu):
     assert_attn_close(got, ref, "prefill_throughput sampled")
 
 
-@pytest.mark.parametrize("Hq,Hkv,D", [(16, 8, 128), (16, 4, 64)])
+@pytest.mark.parametrize("Hq,Hkv,D", [(16, 8, 128), (16, 4, 64), (14, 2, 64), (12, 4, 128)])
 def test_persistent_many_short_sequences(gpu, Hq, Hkv, D):
     """A pack large enough for the persistent form (at least eight 128-row work
-    units per CU) made mostly of short sequences: single-tile items (whose next
-    item is needed before a freshly claimed index is known to have landed),
-    empty sequences and a few long ones.  Every row against the oracle, and two
-    launches bitwise equal."""
+    units per CU; 8, 8, 14 and 12 work units per sequence) made mostly of
+    short sequences: single-tile items (whose next item is needed before a
+    freshly claimed index is known to have landed), empty sequences and a few
+    long ones.  Every row against the oracle, and two launches bitwise equal."""
     rng = np.random.default_rng(11)
     lengths = rng.integers(0, 49, 1600)
     lengths[::97] = 300
