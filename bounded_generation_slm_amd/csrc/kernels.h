@@ -94,17 +94,21 @@ struct TopkParams {
     int32_t* parent;
     float* cum_out;
     uint64_t* stage1;                   // workspace: [R, list_cap] appended stage-1 keys
-    uint64_t* req_thr;                  // workspace: [R] shared thresholds, zero between calls
-    int* req_cnt;                       // workspace: [R] appended key counts, zero between calls
-    int64_t list_cap;                   // keys per request list (>= Win * chunks * W)
+    uint64_t* req_state;                // workspace: [R] x kTopkStateWords (threshold, count), zero between calls
+    int64_t list_cap;                   // keys per request list
+    int64_t seg;                        // candidates per stage-1 wave (a multiple of 4)
     int num_requests, beams_in, vocab, width;
-    int chunks, chunk_len;              // vocabulary chunks per row and their length
 };
 hipError_t launch_beam_topk_merge(const TopkParams& p, hipStream_t stream);
 size_t beam_topk_workspace_bytes(int max_requests, int max_beams);
-int beam_topk_chunks(int num_requests, int beams_in, int vocab, int max_chunks);
-constexpr int kTopkMinItems = 2048;     // stage-1 waves a call aims for
-constexpr int kTopkMaxChunks = 64;      // vocabulary chunks per row at most
+// candidates per stage-1 wave: the call split evenly over the resident waves,
+// at least kTopkMinSegment, and few enough ranges per request for its list
+// (`lists` slots of W keys)
+int64_t beam_topk_segment(int num_requests, int beams_in, int vocab, int64_t resident_waves, int64_t lists);
+int beam_topk_blocks_per_cu(int width);     // resident stage-1 workgroups (4 waves) per CU
+constexpr int64_t kTopkMinSegment = 4096;
+constexpr int kTopkStateWords = 64;     // 512-byte state line per request
+constexpr int kTopkMaxChunks = 64;      // list slots per request at least
 size_t beam_decode_lds_bytes(int head_dim, int prompt_len);
 constexpr int kTopkMaxWidth = 512;
 constexpr int kDecodeMaxSuffix = 8;     // hist_len + 1 <= 8

@@ -24,7 +24,7 @@ struct slm_ctx {
     bool dry_run = false;   // device < 0: validate arguments only, touch no device
     hipStream_t stream = nullptr;
     slm_caps caps{};
-    uint64_t* topk_ws = nullptr;    // [R] shared thresholds, [R] counts (8 B slots), [R] key lists
+    uint64_t* topk_ws = nullptr;    // [R] 512-byte state lines (threshold, count, slots), then [R] key lists
     size_t topk_ws_bytes = 0;
     int64_t topk_lists = 0;         // stage-1 lists (of up to max_beams keys) per request
     int* err_flag = nullptr;
@@ -32,6 +32,7 @@ struct slm_ctx {
     int plan_cap = 0;
     int num_cus = 256;
     size_t max_lds = 0;
+    int topk_blocks_per_cu[slm::kTopkMaxWidth + 1] = {0};   // stage-1 occupancy per width (0 = not queried)
     char last_error[512] = {0};
 };
 
@@ -373,16 +374,16 @@ slm_status slm_beam_topk_merge(slm_ctx* ctx, const float* logprobs, const float*
     slm::TopkParams p{};
     p.logprobs = logprobs; p.cum = cum; p.tokens = tokens; p.parent = parent; p.cum_out = cum_out;
     const int64_t R_cap = ctx->caps.max_requests;
-    p.req_thr = ctx->topk_ws;
-    p.req_cnt = (int*)(ctx->topk_ws + R_cap);
-    p.stage1 = ctx->topk_ws + 2 * R_cap;
+    p.req_state = ctx->topk_ws;
+    p.stage1 = ctx->topk_ws + slm::kTopkStateWords * R_cap;
     p.list_cap = ctx->topk_lists * ctx->caps.max_beams;
     p.num_requests = num_requests; p.beams_in = beams_in; p.vocab = vocab; p.width = width;
-    // lists per request = beams_in * chunks must fit the per-request capacity
-    int chunks = slm::beam_topk_chunks(num_requests, beams_in, vocab,
-                                       (int)std::min<int64_t>(ctx->topk_lists / beams_in, INT32_MAX));
-    p.chunk_len = ((vocab + chunks - 1) / chunks + 3) & ~3;
-    p.chunks = (vocab + p.chunk_len - 1) / p.chunk_len;
+    // stage-1 waves take equal ranges of the flattened candidates, one per
+    // resident wave (four waves per workgroup)
+    int& bpc = ctx->topk_blocks_per_cu[width];
+    if (bpc == 0) bpc = ctx->dry_run ? 1 : slm::beam_topk_blocks_per_cu(width);
+    const int64_t resident = (int64_t)ctx->num_cus * bpc * 4;
+    p.seg = slm::beam_topk_segment(num_requests, beams_in, vocab, resident, ctx->topk_lists);
     return SLM_LAUNCH(ctx, slm::launch_beam_topk_merge(p, ctx->stream), "topk");
 }
 

@@ -225,20 +225,23 @@ __device__ __forceinline__ void insert(SelectorLds& s, const uint64_t (&keys)[kP
         if (keys[e] > thr) s.buf[base + off[e]] = keys[e];
 }
 
-// Bitonic sort of s.buf[0..512) descending (entries >= n padded with 0).
-__device__ void sort_desc_512(SelectorLds& s, int n) {
-    for (int i = threadIdx.x + n; i < kMaxW; i += kTkThreads) s.buf[i] = 0;
+// Bitonic sort of s.buf[0..S) descending, S a power of two <= 512 (entries
+// >= n padded with 0, which ranks below every key).
+__device__ void sort_desc(SelectorLds& s, int n, int S) {
+    for (int i = threadIdx.x + n; i < S; i += kTkThreads) s.buf[i] = 0;
     __syncthreads();
-    for (int size = 2; size <= kMaxW; size <<= 1)
+    for (int size = 2; size <= S; size <<= 1)
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const int t = threadIdx.x;              // 256 threads, one pair each
-            const int i = 2 * t - (t & (stride - 1));
-            const int j = i + stride;
-            const bool desc = (i & size) == 0;
-            const uint64_t a = s.buf[i], b = s.buf[j];
-            if ((a < b) == desc) {
-                s.buf[i] = b;
-                s.buf[j] = a;
+            const int t = threadIdx.x;              // one pair per thread, S / 2 <= 256 pairs
+            if (t < S / 2) {
+                const int i = 2 * t - (t & (stride - 1));
+                const int j = i + stride;
+                const bool desc = (i & size) == 0;
+                const uint64_t a = s.buf[i], b = s.buf[j];
+                if ((a < b) == desc) {
+                    s.buf[i] = b;
+                    s.buf[j] = a;
+                }
             }
             __syncthreads();
         }
@@ -246,6 +249,28 @@ __device__ void sort_desc_512(SelectorLds& s, int n) {
 
 __device__ __forceinline__ uint64_t load_relaxed(const uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Request r's shared state, one 512-byte line of its own (the requests'
+// counters and thresholds land on different memory channels): word 0 the
+// shared threshold, word 1 the appended key count.
+__device__ __forceinline__ uint64_t* req_thr(const TopkParams& p, int r) {
+    return p.req_state + (int64_t)r * kTopkStateWords;
+}
+__device__ __forceinline__ int* req_cnt(const TopkParams& p, int r) {
+    return (int*)(p.req_state + (int64_t)r * kTopkStateWords + 1);
+}
+// Words 32..63: with m = slots(W) slots and q = ceil(W / m), slot s holds
+// the best q-th key that any wave w with w % m == s has held.  m waves with
+// disjoint candidates, each holding q keys at or above its slot's value,
+// together hold m * q >= W keys at or above the smallest slot: that minimum
+// bounds the request's final W-th key from below, and since each slot sees
+// the best of many waves it tracks the W-th key of everything the request's
+// waves have seen so far, far above any one wave's own W-th key.
+constexpr int kSlot0 = 32, kMaxSlots = 32;
+__host__ __device__ inline int topk_slots(int W) { return min(kMaxSlots, max(1, (W + 7) / 8)); }
+__device__ __forceinline__ uint64_t* req_slot(const TopkParams& p, int r, int s) {
+    return p.req_state + (int64_t)r * kTopkStateWords + kSlot0 + s;
 }
 
 // ---- stage 1: one wave per (request, beam row, vocabulary chunk) ----
@@ -265,7 +290,7 @@ constexpr int kWBins = 256;
 
 // LDS layout of one wave, in 8-byte words: buf[soft + kWRound], surv[even(W)],
 // hist[kWBins] ints.
-__host__ __device__ inline int wave_soft_cap(int W) { return W > 256 ? 512 : 256; }
+__host__ __device__ inline int wave_soft_cap(int W) { return W > 512 ? 2 * W : 512; }
 __host__ __device__ inline int wave_lds_words(int W) {
     return wave_soft_cap(W) + kWRound + ((W + 1) & ~1) + kWBins / 2;
 }
@@ -386,118 +411,265 @@ __device__ uint64_t wave_compact(uint64_t* buf, uint64_t* surv, int* hist, int& 
     return kth;
 }
 
+// Shared lower bound of request r's W-th key: lane l < m reads slot l, the
+// other lanes word 0 (the best single-wave W-th key).
+__device__ __forceinline__ const uint64_t* bound_addr(const TopkParams& p, int r, int lane, int m) {
+    return p.req_state + (int64_t)r * kTopkStateWords + (lane < m ? kSlot0 + lane : 0);
+}
+__device__ __forceinline__ uint64_t bound_issue(const TopkParams& p, int r, int lane, int m) {
+    return load_relaxed(bound_addr(p, r, lane, m));
+}
+__device__ __forceinline__ uint64_t bound_take(uint64_t v, int lane, int m) {
+    uint64_t s = lane < m ? v : ~0ull;
+#pragma unroll
+    for (int off = 1; off < kMaxSlots; off <<= 1) {                 // lanes 0..31 hold every slot
+        const uint64_t y = __shfl_xor(s, off);
+        s = y < s ? y : s;
+    }
+    const uint64_t slots = uniform_u64(s);                          // lane 0: min over the slots
+    const uint64_t w0 = ((uint64_t)__builtin_amdgcn_readlane((int)(v >> 32), 63) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);   // lane 63 >= m
+    return slots > w0 ? slots : w0;
+}
+
+// A key threshold from one round: the W-th largest of its valid candidates'
+// order-preserving score bits, truncated to the top 16 (sign, exponent, 7
+// mantissa bits).  At least W of the round's candidates have a key above it,
+// so it bounds the request's final W-th key from below.  0 (no bound) when
+// fewer than W are valid.  A bitwise search counted with ballots: no LDS,
+// one pass over the registers per bit.
+__device__ __forceinline__ uint64_t round_bound(const float (&sc)[kWPerLane], const bool (&valid)[kWPerLane],
+                                                int W) {
+    uint32_t o[kWPerLane];
+    int nvalid = 0;
+#pragma unroll
+    for (int k = 0; k < kWPerLane; ++k) {
+        o[k] = valid[k] ? order_f32(sc[k]) : 0u;
+        nvalid += __popcll(__ballot(valid[k]));
+    }
+    if (nvalid < W) return 0ull;
+    uint32_t tv = 0;
+    for (int b = 31; b >= 16; --b) {
+        const uint32_t cand = tv | (1u << b);
+        int n = 0;
+#pragma unroll
+        for (int k = 0; k < kWPerLane; ++k) n += __popcll(__ballot(o[k] >= cand));
+        if (n >= W) tv = cand;
+    }
+    // tv: the W-th largest of the scores' top 16 order bits, so at least W
+    // candidates have order >= tv; it is nonzero (order(-inf) > 2^16)
+    return ((uint64_t)tv << 32) - 1ull;
+}
+
+// Vector-memory operations of the streaming loop are issued directly, so
+// that the compiler neither tracks nor waits for them: each round waits for
+// exactly its own loads (four rounds stay in flight), where compiler-placed
+// waits merged over the rare insertion path drain the pipeline.  Registers
+// they fill are pinned after the wait that covers them.
+__device__ __forceinline__ f32x4 stream_load16(const float* p) {
+    f32x4 r;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
+__device__ __forceinline__ float stream_load4(const float* p) {
+    float r;
+    asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
+// agent-coherent 8-byte load (the shared bounds are written by atomics of other CUs)
+__device__ __forceinline__ uint64_t coherent_load8(const uint64_t* p) {
+    uint64_t r;
+    asm volatile("global_load_dwordx2 %0, %1, off sc1" : "=v"(r) : "v"(p) : "memory");
+    return r;
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+template <class T>
+__device__ __forceinline__ void pin(T& x) {
+    asm volatile("" : "+v"(x));
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(kTkThreads) void topk_stage1_kernel(const TopkParams p) {
     extern __shared__ __attribute__((aligned(16))) uint64_t wave_lds[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t item = (int64_t)blockIdx.x * (kTkThreads / kWLanes) + wave;
-    const int64_t items = (int64_t)p.num_requests * p.beams_in * p.chunks;
-    if (item >= items) return;                      // no barriers below: waves are independent
-    const int W = p.width;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t wid = (int64_t)blockIdx.x * (kTkThreads / kWLanes) + wave;
+    const int V = p.vocab, W = p.width;
+    const int64_t req_len = (int64_t)p.beams_in * V;           // candidates of one request
+    const int64_t total = (int64_t)p.num_requests * req_len;
+    int64_t a = wid * p.seg;                                    // this wave's range [a, end)
+    if (a >= total) return;                                     // no barriers below: waves are independent
+    const int64_t end = min(total, a + p.seg);
     uint64_t* buf = wave_lds + (size_t)wave * wave_lds_words(W);
     const int soft = wave_soft_cap(W);
     uint64_t* surv = buf + soft + kWRound;
     int* hist = (int*)(surv + ((W + 1) & ~1));
 
-    const int chunk = (int)(item % p.chunks);
-    const int64_t row = item / p.chunks;            // r * Win + b
-    const int r = (int)(row / p.beams_in), b = (int)(row % p.beams_in);
-    const int V = p.vocab;
-    const int v_begin = chunk * p.chunk_len;
-    const int v_end = min(V, v_begin + p.chunk_len);
-    const float* lp = p.logprobs + row * V;
-    const float c = p.cum[row];
-    const uint32_t fbase = (uint32_t)b * (uint32_t)V;
-    // start from the request's shared threshold: the best W-th key any
-    // finished chunk of this request has published (a lower bound of the
-    // request's final W-th key, so filtering with it is exact)
-    uint64_t thr = uniform_u64(__hip_atomic_load(p.req_thr + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    int r = (int)(a / req_len);
+    const int m_slots = topk_slots(W);
+    uint64_t thr = bound_take(bound_issue(p, r, lane, m_slots), lane, m_slots);  // keys > thr pass
+    uint64_t pub = 0, pubq = 0;                                 // last W-th / q-th keys published for r
+    const int q = (W + m_slots - 1) / m_slots;
+    const int slot = (int)(wid % m_slots);
     int cnt = 0;
 
-    const int n = v_end - v_begin;
-    const int rounds = (n + kWRound - 1) / kWRound;
+    // Keep the W largest keys, raise the threshold to the W-th and publish
+    // it (this wave alone holds W keys at or above it, so it bounds request
+    // r's final W-th key from below) and the q-th of them to the wave's slot.
+    // The atomics are waited for at once, so the stream's counts stay exact.
+    auto shrink = [&]() {
+        wave_fence();
+        const uint64_t own = wave_compact(buf, surv, hist, cnt, W, lane);
+        thr = own > thr ? own : thr;
+        const uint64_t oq = q < W ? wave_select_kth(buf, hist, W, q, lane) : own;
+        wave_fence();
+        if (own > pub && lane == 0) atomicMax((unsigned long long*)req_thr(p, r), (unsigned long long)own);
+        if (oq > pubq && lane == 0) atomicMax((unsigned long long*)req_slot(p, r, slot), (unsigned long long)oq);
+        pub = own > pub ? own : pub;
+        pubq = oq > pubq ? oq : pubq;
+        vm_wait<0>();
+    };
+    // Append the keys not below request r's shared threshold to its list.
+    auto count_keep = [&](uint64_t gu) {
+        int k = 0;
+        for (int i0 = 0; i0 < cnt; i0 += kWLanes) {
+            const int i = i0 + lane;
+            k += __popcll(__ballot(i < cnt && buf[i] >= gu));
+        }
+        return k;
+    };
+    auto flush = [&]() {
+        wave_fence();
+        uint64_t gu = bound_take(bound_issue(p, r, lane, m_slots), lane, m_slots);
+        int n_keep = count_keep(gu);
+        if (n_keep > W) {                                       // at most W keys per flush (list capacity)
+            shrink();
+            gu = thr > gu ? thr : gu;
+            n_keep = count_keep(gu);
+        }
+        int base = 0;
+        if (lane == 0 && n_keep > 0) base = atomicAdd(req_cnt(p, r), n_keep);
+        base = __shfl(base, 0);
+        uint64_t* list = p.stage1 + (int64_t)r * p.list_cap;
+        for (int i0 = 0; i0 < cnt; i0 += kWLanes) {
+            const int i = i0 + lane;
+            const bool keep = i < cnt && buf[i] >= gu;
+            const uint64_t m = __ballot(keep);
+            if (keep) list[base + lanes_below(m)] = buf[i];
+            base += __popcll(m);
+        }
+        wave_fence();
+        cnt = 0;
+    };
+
     constexpr int NV = kWPerLane / 4;
-    f32x4 B0[NV], B1[NV], B2[NV], B3[NV];
-    auto fetch = [&](int rd, f32x4 (&dst)[NV]) {
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int v0 = v_begin + rd * kWRound + (j * kWLanes + lane) * 4;
-            if (VEC) {
-                dst[j] = *(const f32x4*)(lp + min(v0, v_end - 4));
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dst[j][e] = lp[min(v0 + e, v_end - 1)];
-            }
+    constexpr int LPF = VEC ? NV : kWPerLane;                   // load instructions per round
+    while (a < end) {
+        const int64_t row = a / V;                              // r * Win + b
+        const int rr = (int)(row / p.beams_in);
+        if (rr != r) {                                          // the range enters the next request
+            flush();
+            r = rr;
+            thr = bound_take(bound_issue(p, r, lane, m_slots), lane, m_slots);
+            pub = 0;
+            pubq = 0;
         }
-    };
-    auto round = [&](int rd, const f32x4 (&src)[NV]) {
-        const float ts = thr_score(thr);
-        float sc[kWPerLane];
-        bool maybe = false;
+        const int64_t pe = min(end, (row + 1) * V);             // this piece: [a, pe) inside one row
+        const int n = (int)(pe - a);
+        const float* lp = p.logprobs + a;
+        const float c = p.cum[row];
+        const uint32_t f0 = (uint32_t)(a - (int64_t)r * req_len);   // flat index b*V + v of lp[0]
+        const uint64_t* baddr = bound_addr(p, r, lane, m_slots);
+        const int rounds = (n + kWRound - 1) / kWRound;
+        vm_wait<0>();                                           // nothing of earlier pieces stays in flight
+        f32x4 B0[NV], B1[NV], B2[NV], B3[NV];
+        // loads of round rd (clamped into the piece: rounds past its end
+        // re-read valid addresses, and their values are never used)
+        auto fetch = [&](int rd, f32x4 (&dst)[NV]) {
 #pragma unroll
-        for (int j = 0; j < NV; ++j)
+            for (int j = 0; j < NV; ++j) {
+                const int i0 = rd * kWRound + (j * kWLanes + lane) * 4;
+                if (VEC) {
+                    dst[j] = stream_load16(lp + min(i0, n - 4));
+                } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sc[j * 4 + e] = c + src[j][e];      // the candidate score: one fp32 add
-                maybe |= sc[j * 4 + e] >= ts;
+                    for (int e = 0; e < 4; ++e) dst[j][e] = stream_load4(lp + min(i0 + e, n - 1));
+                }
             }
-        if (__ballot(maybe) == 0) return;           // the common case once a threshold is set
-        int tot = 0;
+        };
+        auto round = [&](int rd, f32x4 (&src)[NV]) {
 #pragma unroll
-        for (int j = 0; j < NV; ++j)
+            for (int j = 0; j < NV; ++j) pin(src[j]);
+            float sc[kWPerLane];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int v = v_begin + rd * kWRound + (j * kWLanes + lane) * 4 + e;
-                const uint64_t key = v < v_end ? make_key(sc[j * 4 + e], fbase + (uint32_t)v) : 0ull;
-                const bool pass = key > thr;
-                const uint64_t m = __ballot(pass);
-                if (pass) buf[cnt + tot + lanes_below(m)] = key;
-                tot += __popcll(m);
+            for (int j = 0; j < NV; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sc[j * 4 + e] = c + src[j][e];   // the candidate score: one fp32 add
+            if (rd == 0 && W <= kWRound / 2) {                  // a piece's first round: bound it at once
+                bool valid[kWPerLane];
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) valid[j * 4 + e] = (j * kWLanes + lane) * 4 + e < n;
+                const uint64_t rb = round_bound(sc, valid, W);
+                thr = rb > thr ? rb : thr;
             }
-        cnt += tot;
-        if (cnt > soft) {
-            wave_fence();
-            thr = wave_compact(buf, surv, hist, cnt, W, lane);
+            const float ts = thr_score(thr);
+            bool maybe = false;
+#pragma unroll
+            for (int k = 0; k < kWPerLane; ++k) maybe |= sc[k] >= ts;
+            if (__ballot(maybe) == 0) return;                   // the common case once a threshold is set
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool ok = sc[j * 4 + e] >= ts;
+                    if (__ballot(ok) == 0) continue;            // uniform: no lane has a candidate here
+                    const int i = rd * kWRound + (j * kWLanes + lane) * 4 + e;
+                    const uint64_t key = (ok && i < n) ? make_key(sc[j * 4 + e], f0 + (uint32_t)i) : 0ull;
+                    const bool pass = key > thr;
+                    const uint64_t m = __ballot(pass);
+                    if (pass) buf[cnt + lanes_below(m)] = key;
+                    cnt += __popcll(m);
+                }
+            if (cnt > soft) shrink();
+        };
+        // The shared bound is read once per group of four rounds, issued with
+        // the group's first loads and taken up at its last round.
+        // Issue order per group: F(rd+3) S F(rd+4) F(rd+5) F(rd+6); a round
+        // waits until only the operations issued after its own loads remain.
+        fetch(0, B0);
+        fetch(1, B1);
+        fetch(2, B2);
+        for (int rd = 0; rd < rounds; rd += kWDepth) {
+            fetch(rd + 3, B3);
+            uint64_t sh = coherent_load8(baddr);
+            vm_wait<3 * LPF + 1>();
+            round(rd, B0);
+            if (rd + 1 >= rounds) break;
+            fetch(rd + 4, B0);
+            vm_wait<3 * LPF + 1>();
+            round(rd + 1, B1);
+            if (rd + 2 >= rounds) break;
+            fetch(rd + 5, B1);
+            vm_wait<3 * LPF + 1>();
+            round(rd + 2, B2);
+            if (rd + 3 >= rounds) break;
+            fetch(rd + 6, B2);
+            vm_wait<3 * LPF>();
+            pin(sh);
+            const uint64_t u = bound_take(sh, lane, m_slots);
+            thr = u > thr ? u : thr;
+            round(rd + 3, B3);
         }
-    };
-    fetch(0, B0);
-    fetch(1, B1);
-    fetch(2, B2);
-    for (int rd = 0; rd < rounds; rd += kWDepth) {
-        fetch(rd + 3, B3);
-        round(rd, B0);
-        if (rd + 1 >= rounds) break;
-        fetch(rd + 4, B0);
-        round(rd + 1, B1);
-        if (rd + 2 >= rounds) break;
-        fetch(rd + 5, B1);
-        round(rd + 2, B2);
-        if (rd + 3 >= rounds) break;
-        fetch(rd + 6, B2);
-        round(rd + 3, B3);
+        vm_wait<0>();                                           // loads issued past the piece's end land here
+        a = pe;
     }
-    wave_fence();
-    if (cnt > W) thr = wave_compact(buf, surv, hist, cnt, W, lane);
-    // publish this chunk's W-th key when it alone holds W candidates
-    if (cnt >= W && lane == 0) atomicMax((unsigned long long*)p.req_thr + r, (unsigned long long)thr);
-    const uint64_t gu = uniform_u64(__hip_atomic_load(p.req_thr + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    // append the keys not below the shared threshold to the request's list
-    int total = 0;
-    for (int i0 = 0; i0 < cnt; i0 += kWLanes) {
-        const int i = i0 + lane;
-        total += __popcll(__ballot(i < cnt && buf[i] >= gu));
-    }
-    int base = 0;
-    if (lane == 0 && total > 0) base = atomicAdd(p.req_cnt + r, total);
-    base = __shfl(base, 0);
-    uint64_t* list = p.stage1 + (int64_t)r * p.list_cap;
-    for (int i0 = 0; i0 < cnt; i0 += kWLanes) {
-        const int i = i0 + lane;
-        const bool keep = i < cnt && buf[i] >= gu;
-        const uint64_t m = __ballot(keep);
-        if (keep) list[base + lanes_below(m)] = buf[i];
-        base += __popcll(m);
-    }
+    flush();
 }
 
 // Stage 2: per request, over the keys the chunks appended to its list.
@@ -505,7 +677,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage2_kernel(const TopkParam
     __shared__ SelectorLds s;
     const int r = blockIdx.x;
     const int W = p.width, V = p.vocab;
-    const int n = p.req_cnt[r];
+    const int n = *req_cnt(p, r);
     const uint64_t* in = p.stage1 + (int64_t)r * p.list_cap;
     if (threadIdx.x == 0) {
         s.cnt = 0;
@@ -526,7 +698,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage2_kernel(const TopkParam
         if (s.cnt > kSoftCap) compact(s, W);
     }
     compact(s, W);
-    sort_desc_512(s, min(s.cnt, W));
+    int S = 2;
+    while (S < W) S <<= 1;
+    sort_desc(s, min(s.cnt, W), S);
     for (int j = threadIdx.x; j < W; j += kTkThreads) {
         const uint64_t key = s.buf[j];
         const uint32_t f = 0xFFFFFFFFu - (uint32_t)key;
@@ -535,37 +709,44 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage2_kernel(const TopkParam
         p.cum_out[(int64_t)r * W + j] = unorder_f32((uint32_t)(key >> 32));
     }
     // leave the request's shared state cleared for the next call
-    if (threadIdx.x == 0) {
-        __hip_atomic_store(p.req_thr + r, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(p.req_cnt + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (threadIdx.x < kSlot0 + kMaxSlots)       // words 0..63: threshold, count, slots
+        __hip_atomic_store(p.req_state + (int64_t)r * kTopkStateWords + threadIdx.x, 0ull, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
 
 size_t beam_topk_workspace_bytes(int max_requests, int max_beams) {
-    // per request: a shared threshold (8 B), an append count (4 B, padded to
-    // 8) and a list of up to max(max_beams, kTopkMaxChunks) * max_beams keys
+    // per request: a 512-byte state line (threshold, append count, slots) and
+    // a list of up to max(max_beams, kTopkMaxChunks) * max_beams keys
     const size_t per_req_lists = std::max<size_t>((size_t)max_beams, kTopkMaxChunks);
-    return (size_t)max_requests * (2 + per_req_lists * max_beams) * sizeof(uint64_t);
+    return (size_t)max_requests * (kTopkStateWords + per_req_lists * max_beams) * sizeof(uint64_t);
 }
 
-int beam_topk_chunks(int num_requests, int beams_in, int vocab, int max_chunks) {
-    const int64_t rows = (int64_t)num_requests * beams_in;
-    int64_t c = (kTopkMinItems + rows - 1) / rows;           // enough waves to fill the GPU
-    c = std::min<int64_t>(c, std::max<int64_t>(1, vocab / (8 * kWRound)));  // chunks of 8+ wave rounds
-    c = std::min<int64_t>(c, std::min(max_chunks, kTopkMaxChunks));  // the request's list must hold them
-    return (int)std::max<int64_t>(1, c);
+size_t beam_topk_stage1_lds(int width) {
+    return (size_t)wave_lds_words(width) * sizeof(uint64_t) * (kTkThreads / kWLanes);
+}
+
+int64_t beam_topk_segment(int num_requests, int beams_in, int vocab, int64_t resident_waves, int64_t lists) {
+    const int64_t total = (int64_t)num_requests * beams_in * vocab;
+    const int64_t req_len = (int64_t)beams_in * vocab;
+    int64_t seg = (total + resident_waves - 1) / std::max<int64_t>(1, resident_waves);   // one range per resident wave
+    seg = std::max<int64_t>(seg, kTopkMinSegment);
+    // a request's list takes at most W keys from each range that overlaps it:
+    // ceil(req_len / seg) + 1 ranges must fit its `lists` W-key slots
+    seg = std::max<int64_t>(seg, (req_len + lists - 2) / std::max<int64_t>(1, lists - 1));
+    return (seg + 3) & ~(int64_t)3;                             // whole float4s
 }
 
 hipError_t launch_beam_topk_merge(const TopkParams& p, hipStream_t stream) {
     if (p.num_requests == 0) return hipSuccess;
-    const bool vec = (p.vocab % 4 == 0) && (((uintptr_t)p.logprobs & 15) == 0) && (p.chunk_len % 4 == 0);
+    const bool vec = (p.vocab % 4 == 0) && (((uintptr_t)p.logprobs & 15) == 0);
     // stage 2 resets the shared state it consumed; nothing else touches it
-    const int64_t items = (int64_t)p.num_requests * p.beams_in * p.chunks;
-    const int64_t blocks = (items + kTkThreads / kWLanes - 1) / (kTkThreads / kWLanes);
+    const int64_t total = (int64_t)p.num_requests * p.beams_in * p.vocab;
+    const int64_t waves = (total + p.seg - 1) / p.seg;
+    const int64_t blocks = (waves + kTkThreads / kWLanes - 1) / (kTkThreads / kWLanes);
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-    const size_t lds = (size_t)wave_lds_words(p.width) * sizeof(uint64_t) * (kTkThreads / kWLanes);
+    const size_t lds = beam_topk_stage1_lds(p.width);
     if (vec)
         hipLaunchKernelGGL(topk_stage1_kernel<true>, dim3((unsigned)blocks), dim3(kTkThreads), lds, stream, p);
     else
@@ -577,10 +758,18 @@ hipError_t launch_beam_topk_merge(const TopkParams& p, hipStream_t stream) {
     if (e != hipSuccess) {
         // stage 2 clears the shared state; without it it must not leak into the next call
         (void)hipStreamSynchronize(stream);
-        (void)hipMemset(p.req_thr, 0, sizeof(uint64_t) * (size_t)p.num_requests);
-        (void)hipMemset(p.req_cnt, 0, sizeof(int) * (size_t)p.num_requests);
+        (void)hipMemset(p.req_state, 0, sizeof(uint64_t) * kTopkStateWords * (size_t)p.num_requests);
     }
     return e;
+}
+
+int beam_topk_blocks_per_cu(int width) {
+    int n = 0;
+    const size_t lds = beam_topk_stage1_lds(width);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)topk_stage1_kernel<true>, kTkThreads, lds) !=
+            hipSuccess || n <= 0)
+        n = 1;
+    return n;
 }
 
 }  // namespace slm
