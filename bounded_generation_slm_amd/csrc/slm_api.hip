@@ -314,7 +314,8 @@ slm_status slm_beam_decode_attn(slm_ctx* ctx, const slm_beam_attn_args* a) {
                     a->prompt_len, a->head_dim, lds, ctx->max_lds);
     const size_t NL = a->n_layers, R = a->num_requests, W = a->width, D = a->head_dim;
     const size_t Hq = a->n_heads_q, Hkv = a->n_heads_kv;
-    if ((NL * R * W * Hq) > (size_t)INT32_MAX || NL * R * Hkv * 8 > (size_t)INT32_MAX)
+    if ((NL * R * W * Hq) > (size_t)INT32_MAX || NL * R * Hkv * 8 > (size_t)INT32_MAX ||
+        W * Hq * D * 4 >= (size_t)INT32_MAX)
         return fail(ctx, SLM_ERR_UNSUPPORTED, "decode: too many rows");
     const size_t qb = NL * R * W * Hq * D * 2, ob = NL * R * W * Hq * D * (a->out_dtype == SLM_F32 ? 4 : 2);
     const size_t pb = NL * R * a->prompt_len * Hkv * D * 2, sb = NL * R * W * a->suffix_cap * Hkv * D * 2;
