@@ -17,6 +17,10 @@ resident in HBM:
 value = prefill tokens per step (T, each through all 28 layers) / step time.
 The JSON line also carries the per-part times, the roofline of the dominant
 kernel (packed prefill attention) and the oracle timed on a bounded sample.
+Outside the timed step, the same calls are timed on two more workloads for
+reporting only: one prefill-only request (15 packed samples, one layer, then
+the gather) and the long-prompt wide beam search (8 requests x 400 beams,
+prompt 480, 5 steps).
 """
 from __future__ import annotations
 
@@ -43,6 +47,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the timed oracle sample")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the reporting-only prefill-request and long-prompt beam timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -143,6 +149,133 @@ def traffic_from_counters(kernel_file: str, launch_bytes_key: str):
     return rec.get(launch_bytes_key)
 
 
+def extra_workloads(ctx, dev, ev, reps=5):
+    """Reporting-only timings outside the timed step (not part of value)."""
+    import torch
+    import workloads as wl
+    res = {}
+    # one prefill-only request: 15 packed samples, one layer, then the gather
+    pr = wl.PREFILL_REQUEST
+    T, Hq, Hkv, D = pr.total_tokens, pr.n_heads_q, pr.n_heads_kv, pr.head_dim
+    q = wl.torch_normal_bf16((T, Hq, D), (pr.base_seed, wl.TID_Q, 0, 0), dev)
+    k = wl.torch_normal_bf16((T, Hkv, D), (pr.base_seed, wl.TID_K, 0, 0), dev)
+    v = wl.torch_normal_bf16((T, Hkv, D), (pr.base_seed, wl.TID_V, 0, 0), dev)
+    hidden = wl.torch_normal_bf16((T, pr.hidden_dim), (pr.base_seed, wl.TID_HIDDEN, 0, 0), dev)
+    cu = torch.from_numpy(pr.cu_seqlens()).to(dev)
+    out = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+    g = torch.empty((len(pr.lengths), pr.hidden_dim), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        ctx.packed_prefill_attn(q, k, v, cu, pr.max_seqlen, out=out)
+        ctx.gather_last(hidden, cu, out=g)
+    times = []
+    for _ in range(reps * 4):
+        e0 = ev()
+        ctx.packed_prefill_attn(q, k, v, cu, pr.max_seqlen, out=out)
+        ctx.gather_last(hidden, cu, out=g)
+        times.append((e0, ev()))
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in times)[len(times) // 2]
+    pbytes, pflops = prefill_bytes_flops(pr.lengths, Hq, Hkv, D, 4)
+    res["prefill_request"] = {
+        "workload": "15 packed samples U[64,500] (T=%d), Hq16/Hkv8/D128, fp32 out, 1 layer + gather [T,1024]" % T,
+        "us_per_request_median": round(us, 1), "tokens_per_s": round(T / (us * 1e-6), 1),
+        "hbm_frac": round(pbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(pflops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    del q, k, v, hidden, out
+    # the long-prompt wide beam search
+    bl = BeamRun(wl.BEAM_LONG, dev)
+    bl.run(ctx, [], ev)
+    marks = []
+    for _ in range(reps):
+        bl.run(ctx, marks, ev)
+    torch.cuda.synchronize()
+    per = {}
+    for name, a, b in marks:
+        per.setdefault(name, []).append(a.elapsed_time(b) * 1e3)
+    res["beam_long_prompt"] = dict(
+        {"workload": "R8 x W400, P480, 5 steps, 24 layers, Hq14/Hkv2/D64, V151936"}, **bl.summary(per))
+    del bl
+    torch.cuda.empty_cache()
+    return {"reporting_only": res}
+
+
+class BeamRun:
+    """Device-resident inputs of one fixed-step beam search and its launch
+    sequence: first merge (one beam in), then per step the all-layer decode
+    attention (history read through the last parents, suffix written in the
+    new order) and the merge, finally the suffix reorder by the last parents."""
+
+    def __init__(self, bs, dev):
+        import torch
+        import workloads as wl
+        self.bs = bs
+        NL, R, W, P, N, V = bs.n_layers, bs.num_requests, bs.width, bs.prompt_len, bs.n_steps, bs.vocab
+        Hq, Hkv, D = bs.n_heads_q, bs.n_heads_kv, bs.head_dim
+        self.pk = wl.torch_normal_bf16((NL, R, P, Hkv, D), (bs.base_seed, wl.TID_PREFIX_K, 0, 0), dev)
+        self.pv = wl.torch_normal_bf16((NL, R, P, Hkv, D), (bs.base_seed, wl.TID_PREFIX_V, 0, 0), dev)
+        steps = range(1, N + 1)
+        self.q = [None] + [wl.torch_normal_bf16((NL, R, W, Hq, D), (bs.base_seed, wl.TID_Q, 0, t), dev) for t in steps]
+        self.kn = [None] + [wl.torch_normal_bf16((NL, R, W, Hkv, D), (bs.base_seed, wl.TID_K_NEW, 0, t), dev)
+                            for t in steps]
+        self.vn = [None] + [wl.torch_normal_bf16((NL, R, W, Hkv, D), (bs.base_seed, wl.TID_V_NEW, 0, t), dev)
+                            for t in steps]
+        self.lps = [wl.torch_logprobs((R, 1 if t == 0 else W, V), (bs.base_seed, wl.TID_LOGITS, 0, t), dev)
+                    for t in range(N + 1)]
+        self.cum0 = torch.zeros((R, 1), dtype=torch.float32, device=dev)
+        self.toks = [torch.empty((R, W), dtype=torch.int32, device=dev) for _ in range(N + 1)]
+        self.pars = [torch.empty((R, W), dtype=torch.int32, device=dev) for _ in range(N + 1)]
+        self.cums = [torch.empty((R, W), dtype=torch.float32, device=dev) for _ in range(N + 1)]
+        sshape = (NL, R, W, bs.suffix_cap, Hkv, D)
+        self.suf = [(torch.zeros(sshape, dtype=torch.bfloat16, device=dev),
+                     torch.zeros(sshape, dtype=torch.bfloat16, device=dev)) for _ in range(3)]
+        self.out = torch.empty((NL, R, W, Hq, D), dtype=torch.float32, device=dev)
+
+    def run(self, ctx, marks, ev):
+        bs, N, W = self.bs, self.bs.n_steps, self.bs.width
+        e0 = ev()
+        ctx.beam_topk_merge(self.lps[0], self.cum0, W, self.toks[0], self.pars[0], self.cums[0])
+        marks.append(("merge0", e0, ev()))
+        for t in range(1, N + 1):
+            (ski, svi), (sko, svo) = self.suf[(t + 1) % 2], self.suf[t % 2]
+            e0 = ev()
+            ctx.beam_decode_attn(self.q[t], self.pk, self.pv, ski if t > 1 else None, svi if t > 1 else None,
+                                 self.kn[t], self.vn[t], self.pars[t - 1], t - 1, sko, svo, out=self.out)
+            e1 = ev()
+            ctx.beam_topk_merge(self.lps[t], self.cums[t - 1], W, self.toks[t], self.pars[t], self.cums[t])
+            e2 = ev()
+            marks.append(("decode%d" % t, e0, e1))
+            marks.append(("merge%d" % t, e1, e2))
+        e0 = ev()
+        ctx.beam_reorder_suffix(self.pars[N], self.suf[N % 2][0], self.suf[N % 2][1], N, self.suf[2][0],
+                                self.suf[2][1])
+        marks.append(("reorder", e0, ev()))
+
+    def summary(self, per):
+        """Per-part averages (us) and the beam-step HBM fraction."""
+        bs = self.bs
+        N, R, W, V = bs.n_steps, bs.num_requests, bs.width, bs.vocab
+        avg = {k: sum(v) / len(v) for k, v in per.items()}
+        parts = ["merge0"] + ["decode%d" % t for t in range(1, N + 1)] + ["merge%d" % t for t in range(1, N + 1)] \
+            + ["reorder"]
+        search_us = sum(avg[p] for p in parts)
+        step_us = [avg["decode%d" % t] + avg["merge%d" % t] for t in range(1, N + 1)]
+        step_bytes = [decode_bytes(bs, t) + topk_bytes(R, W, V, W) for t in range(1, N + 1)]
+        return {
+            "beam_search_us": round(search_us, 1),
+            "beam_step_us": [round(u, 1) for u in step_us],
+            "beam_step_us_mean": round(sum(step_us) / N, 1),
+            "beam_step_hbm_frac": [round(b / (u * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) for b, u in zip(step_bytes, step_us)],
+            "decode_us": [round(avg["decode%d" % t], 1) for t in range(1, N + 1)],
+            "decode_hbm_frac": [round(decode_bytes(bs, t) / (avg["decode%d" % t] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                for t in range(1, N + 1)],
+            "merge_us": [round(avg["merge%d" % t], 1) for t in range(0, N + 1)],
+            "merge_hbm_frac": [round(topk_bytes(R, W, V, W) / (avg["merge%d" % t] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                               for t in range(1, N + 1)],
+            "reorder_us": round(avg["reorder"], 1),
+            "beam_requests_per_s": round(R / (search_us * 1e-6), 1),
+        }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -181,22 +314,7 @@ def main():
     pout = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
     gout = torch.empty((len(pf.lengths), pf.hidden_dim), dtype=torch.bfloat16, device=dev)
 
-    NL, R, W, P, N, V = bs.n_layers, bs.num_requests, bs.width, bs.prompt_len, bs.n_steps, bs.vocab
-    bHq, bHkv, bD = bs.n_heads_q, bs.n_heads_kv, bs.head_dim
-    pk = wl.torch_normal_bf16((NL, R, P, bHkv, bD), (bs.base_seed, wl.TID_PREFIX_K, 0, 0), dev)
-    pv = wl.torch_normal_bf16((NL, R, P, bHkv, bD), (bs.base_seed, wl.TID_PREFIX_V, 0, 0), dev)
-    bq = [None] + [wl.torch_normal_bf16((NL, R, W, bHq, bD), (bs.base_seed, wl.TID_Q, 0, t), dev) for t in range(1, N + 1)]
-    kn = [None] + [wl.torch_normal_bf16((NL, R, W, bHkv, bD), (bs.base_seed, wl.TID_K_NEW, 0, t), dev) for t in range(1, N + 1)]
-    vn = [None] + [wl.torch_normal_bf16((NL, R, W, bHkv, bD), (bs.base_seed, wl.TID_V_NEW, 0, t), dev) for t in range(1, N + 1)]
-    lps = [wl.torch_logprobs((R, 1 if t == 0 else W, V), (bs.base_seed, wl.TID_LOGITS, 0, t), dev) for t in range(N + 1)]
-    cum0 = torch.zeros((R, 1), dtype=torch.float32, device=dev)
-    toks = [torch.empty((R, W), dtype=torch.int32, device=dev) for _ in range(N + 1)]
-    pars = [torch.empty((R, W), dtype=torch.int32, device=dev) for _ in range(N + 1)]
-    cums = [torch.empty((R, W), dtype=torch.float32, device=dev) for _ in range(N + 1)]
-    sshape = (NL, R, W, bs.suffix_cap, bHkv, bD)
-    suf = [(torch.zeros(sshape, dtype=torch.bfloat16, device=dev), torch.zeros(sshape, dtype=torch.bfloat16, device=dev))
-           for _ in range(3)]
-    bout = torch.empty((NL, R, W, bHq, bD), dtype=torch.float32, device=dev)
+    beam = BeamRun(bs, dev)
     torch.cuda.synchronize()
 
     def ev():
@@ -213,22 +331,7 @@ def main():
         e0 = ev()
         ctx.gather_last(hidden, cu, out=gout)
         marks.append(("gather", e0, ev()))
-        e0 = ev()
-        ctx.beam_topk_merge(lps[0], cum0, W, toks[0], pars[0], cums[0])
-        marks.append(("merge0", e0, ev()))
-        for t in range(1, N + 1):
-            (ski, svi), (sko, svo) = suf[(t + 1) % 2], suf[t % 2]
-            e0 = ev()
-            ctx.beam_decode_attn(bq[t], pk, pv, ski if t > 1 else None, svi if t > 1 else None, kn[t], vn[t],
-                                 pars[t - 1], t - 1, sko, svo, out=bout)
-            e1 = ev()
-            ctx.beam_topk_merge(lps[t], cums[t - 1], W, toks[t], pars[t], cums[t])
-            e2 = ev()
-            marks.append(("decode%d" % t, e0, e1))
-            marks.append(("merge%d" % t, e1, e2))
-        e0 = ev()
-        ctx.beam_reorder_suffix(pars[N], suf[N % 2][0], suf[N % 2][1], N, suf[2][0], suf[2][1])
-        marks.append(("reorder", e0, ev()))
+        beam.run(ctx, marks, ev)
 
     for _ in range(args.warmup):
         step([])
@@ -253,18 +356,14 @@ def main():
     per = {}
     for name, a, b in marks:
         per.setdefault(name, []).append(a.elapsed_time(b) * 1e3)   # us
-    avg = {kk: sum(vv) / len(vv) for kk, vv in per.items()}
-    prefill_us = avg["prefill"]
-    beam_parts = ["merge0"] + ["decode%d" % t for t in range(1, N + 1)] + ["merge%d" % t for t in range(1, N + 1)] + ["reorder"]
-    beam_search_us = sum(avg[p] for p in beam_parts)
-    step_us = [avg["decode%d" % t] + avg["merge%d" % t] for t in range(1, N + 1)]
+    prefill_us = sum(per["prefill"]) / len(per["prefill"])
+    gather_us = sum(per["gather"]) / len(per["gather"])
 
     pbytes, pflops = prefill_bytes_flops(pf.lengths, Hq, Hkv, D, 4)
     achieved_gbs = pbytes / (prefill_us * 1e-6) / 1e9
     mfma_tflops = pflops / (prefill_us * 1e-6) / 1e12
-    step_bytes = [decode_bytes(bs, t) + topk_bytes(R, W, V, W) for t in range(1, N + 1)]
-    step_gbs = [b / (u * 1e-6) / 1e9 for b, u in zip(step_bytes, step_us)]
     traffic = traffic_from_counters("prefill_attn.hip", "hbm_bytes_per_launch")
+    extra = {} if args.no_extra else extra_workloads(ctx, dev, ev)
 
     value = pf.total_tokens / (ms_step * 1e-3)
     line = {
@@ -301,22 +400,14 @@ def main():
             "mfma_frac_ceiling_at_hbm_peak": round(min(1.0, pflops / pbytes * HBM_PEAK_GBS * 1e9 / 1e12
                                                        / MFMA_BF16_PEAK_TFLOPS), 4),
         },
-        "parts": {
+        "parts": dict({
             "prefill_layer_us": round(prefill_us, 2),
             "prefill_28_layers_ms": round(prefill_us * pf.n_layers / 1e3, 3),
             "prefill_tokens_per_s": round(pf.total_tokens / (prefill_us * pf.n_layers * 1e-6), 1),
-            "gather_us": round(avg["gather"], 2),
-            "beam_search_us": round(beam_search_us, 1),
-            "beam_step_us": [round(u, 1) for u in step_us],
-            "beam_step_us_mean": round(sum(step_us) / N, 1),
-            "beam_step_hbm_frac": [round(g / HBM_PEAK_GBS, 4) for g in step_gbs],
-            "decode_us": [round(avg["decode%d" % t], 1) for t in range(1, N + 1)],
-            "merge_us": [round(avg["merge%d" % t], 1) for t in range(0, N + 1)],
-            "reorder_us": round(avg["reorder"], 1),
-            "beam_requests_per_s": round(R / (beam_search_us * 1e-6), 1),
-            "host_wall_s": round(t_wall, 3),
-        },
+            "gather_us": round(gather_us, 2),
+        }, **beam.summary(per), host_wall_s=round(t_wall, 3)),
     }
+    line.update(extra)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pf, bs)
     print(json.dumps(line), flush=True)
