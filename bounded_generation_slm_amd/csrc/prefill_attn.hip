@@ -398,6 +398,7 @@ struct PersistentTask {
     bool need_next;                             // iu is fully issued: start item ki + 1 at the next call
     bool idone;                                 // no item after iu
     int ih0, ih1;                               // list index of items ki, ki - 1
+    PItem iu1;                                  // item ki - 1 (valid when ih1 indexes the list)
     // compute side
     PItem cu;
     int jc, tc, h, wrow0, qrow, last_tile;
@@ -443,6 +444,7 @@ struct PersistentTask {
             ki = want;
             ih1 = ih0;
             ih0 = idx;
+            iu1 = iu;                           // item ki - 1, decoded when it started
             if (idx < cnt) {
                 iu = decode(idx);
                 ti = 0;
@@ -544,14 +546,22 @@ struct PersistentTask {
         fresh = false;
         ++step_no;
         if (++tc == cu.ntiles) {
-            // the issue side has started item jc + 1 and at most one more
+            // the issue side has started item jc + 1 and at most one more;
+            // take the item as the issue side decoded it
+            const bool sel0 = ki == jc + 1;
             const int a0 = opaque_uniform(ih0), a1 = opaque_uniform(ih1);
-            const int nidx = ki == jc + 1 ? a0 : a1;
+            const int nidx = sel0 ? a0 : a1;
             const bool more = nidx >= 0 && nidx < cnt;
             const PItem fin = cu;
             const int fin_wrow0 = wrow0, fin_h = h;
             if (more) {
-                cu = decode(nidx);
+                const PItem& nu = sel0 ? iu : iu1;
+                cu.s0 = __builtin_amdgcn_readfirstlane(nu.s0);   // uniform by construction
+                cu.L = __builtin_amdgcn_readfirstlane(nu.L);
+                cu.q0 = __builtin_amdgcn_readfirstlane(nu.q0);
+                cu.ntiles = __builtin_amdgcn_readfirstlane(nu.ntiles);
+                cu.g = __builtin_amdgcn_readfirstlane(nu.g);
+                cu.h0 = __builtin_amdgcn_readfirstlane(nu.h0);
                 bind();
             }
             epilogue(fin, fin_wrow0, fin_h);    // ST ops
@@ -617,6 +627,7 @@ __global__ __launch_bounds__(256, 2) void prefill_persistent_kernel(const Prefil
     T.idone = false;
     T.ih0 = l;
     T.ih1 = -1;
+    T.iu1 = T.iu;
     T.cu = T.iu;
     T.jc = 0;
     T.tc = 0;
