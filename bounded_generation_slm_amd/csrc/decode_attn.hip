@@ -7,8 +7,9 @@
 // head h the keys are the P prompt rows of its request, the history rows of
 // its parent beam and its own new row, all visible.
 //
-// Work decomposition: a workgroup (8 waves) owns one (layer, request, KV
-// head, chunk of query rows).  The query rows of a (layer, request, KV head)
+// Work decomposition: a workgroup (8 waves; 16 when the prompt's LDS copy is
+// too large for two workgroups per CU) owns one (layer, request, KV head,
+// chunk of query rows).  The query rows of a (layer, request, KV head)
 // are the W beams x G query heads of the group, stacked in the MFMA M
 // dimension (row m = beam * G + head-in-group).  The prompt K and V^T of the
 // unit are staged in LDS once per workgroup and reused by every 32-row block,
@@ -24,7 +25,7 @@
 namespace slm {
 namespace {
 
-constexpr int kDecThreads = 512;
+constexpr size_t kDecSmallLds = 80 * 1024;     // two workgroups per CU fit
 
 template <int D>
 struct DecodeLds {
@@ -36,8 +37,8 @@ struct DecodeLds {
     }
 };
 
-template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(kDecThreads, 1) void beam_decode_attn_kernel(const DecodeParams p,
+template <int D, bool OUT_BF16, int NTHR>
+__global__ __launch_bounds__(NTHR) void beam_decode_attn_kernel(const DecodeParams p,
                                                                           int chunks, int chunk_rows) {
     constexpr int NKS = D / 16, NDB = D / 32, KROW = D + 8;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -71,14 +72,14 @@ __global__ __launch_bounds__(kDecThreads, 1) void beam_decode_attn_kernel(const 
         const uint16_t* pk = p.prefix_k + (int64_t)lr * P * kv_row + (int64_t)g * D;
         const uint16_t* pv = p.prefix_v + (int64_t)lr * P * kv_row + (int64_t)g * D;
         const int kchunks = PP * (D / 8);
-        for (int c = tid; c < kchunks; c += kDecThreads) {
+        for (int c = tid; c < kchunks; c += NTHR) {
             const int key = c / (D / 8), dg = c % (D / 8);
             const u32x4 x = key < P ? *(const u32x4*)(pk + key * kv_row + dg * 8) : u32x4{0u, 0u, 0u, 0u};
             *(u32x4*)(k_lds + key * KROW + dg * 8) = x;
         }
         // V^T: unit = (16-key chunk c16, half vh, d-group dg); keys 16c16 + 8(e/4) + 4vh + e%4
         const int vunits = (PP / 16) * 2 * (D / 8);
-        for (int u = tid; u < vunits; u += kDecThreads) {
+        for (int u = tid; u < vunits; u += NTHR) {
             const int c8 = u % ((PP / 16) * 2), dg = u / ((PP / 16) * 2);
             const int c16 = c8 >> 1, vh = c8 & 1;
             u32x4 vb[8];
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void beam_decode_attn_kernel(const 
         const int rows_out = p.hist_len + 1;
         const int cpr = D / 8;                                          // 16-byte chunks per row
         const int total = (wb1 - wb0) * rows_out * cpr;
-        for (int c = tid; c < total; c += kDecThreads) {
+        for (int c = tid; c < total; c += NTHR) {
             const int part = c % cpr;
             const int i = (c / cpr) % rows_out;
             const int w = wb0 + c / (cpr * rows_out);
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void beam_decode_attn_kernel(const 
     __syncthreads();
 
     const int nkc = PP / 64;                      // 64-key prompt chunks
-    for (int blk = row0 + wave * 32; blk < row1; blk += 32 * (kDecThreads / kWave)) {
+    for (int blk = row0 + wave * 32; blk < row1; blk += 32 * (NTHR / kWave)) {
         const int m = blk + n;                    // this lane's query row
         const bool valid = m < row1;
         const int w = valid ? m / G : 0;
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void beam_decode_attn_kernel(const 
     }
 }
 
-template <int D, bool OUT_BF16>
+template <int D, bool OUT_BF16, int NTHR>
 hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
     const int n_units = p.n_layers * p.num_requests * p.n_heads_kv;
     const int M = p.width * p.group;
@@ -302,10 +303,10 @@ hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
     const int64_t blocks = units_padded * chunks;
     if (blocks == 0) return hipSuccess;
     const size_t lds = DecodeLds<D>::bytes(p.prompt_len);
-    auto kern = beam_decode_attn_kernel<D, OUT_BF16>;
+    auto kern = beam_decode_attn_kernel<D, OUT_BF16, NTHR>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kDecThreads), lds, stream, p, chunks, chunk_rows);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NTHR), lds, stream, p, chunks, chunk_rows);
     return hipGetLastError();
 }
 
@@ -317,9 +318,13 @@ size_t beam_decode_lds_bytes(int head_dim, int prompt_len) {
 
 hipError_t launch_beam_decode_attn(const DecodeParams& p, int head_dim, bool out_bf16,
                                    hipStream_t stream) {
+    // A prompt copy too large for two workgroups per CU is shared by 16 waves
+    // (head_dim 64; at 128 the registers of 16 waves would not hold a lane's state).
+    const bool wide = head_dim == 64 && beam_decode_lds_bytes(head_dim, p.prompt_len) > kDecSmallLds;
     if (head_dim == 128)
-        return out_bf16 ? launch_variant<128, true>(p, stream) : launch_variant<128, false>(p, stream);
-    return out_bf16 ? launch_variant<64, true>(p, stream) : launch_variant<64, false>(p, stream);
+        return out_bf16 ? launch_variant<128, true, 512>(p, stream) : launch_variant<128, false, 512>(p, stream);
+    return out_bf16 ? (wide ? launch_variant<64, true, 1024>(p, stream) : launch_variant<64, true, 512>(p, stream))
+                    : (wide ? launch_variant<64, false, 1024>(p, stream) : launch_variant<64, false, 512>(p, stream));
 }
 
 }  // namespace slm
