@@ -517,21 +517,26 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage1_kernel(const TopkParam
     const int slot = (int)(wid % m_slots);
     int cnt = 0;
 
-    // Keep the W largest keys, raise the threshold to the W-th and publish
-    // it (this wave alone holds W keys at or above it, so it bounds request
-    // r's final W-th key from below) and the q-th of them to the wave's slot.
-    // The atomics are waited for at once, so the stream's counts stay exact.
+    // Publish a W-th-key bound to word 0 and a q-th-key bound to this wave's
+    // slot (each backed by that many of this wave's candidates at or above
+    // it).  The atomics return nothing; in the stream's waits, which count
+    // only loads issued after the awaited ones (and loads return in order),
+    // they can only make a wait stricter.
+    auto publish = [&](uint64_t own, uint64_t oq) {
+        if (own > pub && lane == 0) atomicMax((unsigned long long*)req_thr(p, r), (unsigned long long)own);
+        if (oq > pubq && lane == 0) atomicMax((unsigned long long*)req_slot(p, r, slot), (unsigned long long)oq);
+        pub = own > pub ? own : pub;
+        pubq = oq > pubq ? oq : pubq;
+    };
+    // Keep the W largest keys, raise the threshold to the W-th and publish it
+    // and the q-th of them.
     auto shrink = [&]() {
         wave_fence();
         const uint64_t own = wave_compact(buf, surv, hist, cnt, W, lane);
         thr = own > thr ? own : thr;
         const uint64_t oq = q < W ? wave_select_kth(buf, hist, W, q, lane) : own;
         wave_fence();
-        if (own > pub && lane == 0) atomicMax((unsigned long long*)req_thr(p, r), (unsigned long long)own);
-        if (oq > pubq && lane == 0) atomicMax((unsigned long long*)req_slot(p, r, slot), (unsigned long long)oq);
-        pub = own > pub ? own : pub;
-        pubq = oq > pubq ? oq : pubq;
-        vm_wait<0>();
+        publish(own, oq);
     };
     // Append the keys not below request r's shared threshold to its list.
     auto count_keep = [&](uint64_t gu) {
@@ -616,7 +621,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage1_kernel(const TopkParam
 #pragma unroll
                     for (int e = 0; e < 4; ++e) valid[j * 4 + e] = (j * kWLanes + lane) * 4 + e < n;
                 const uint64_t rb = round_bound(sc, valid, W);
+                const uint64_t rq = q < W ? round_bound(sc, valid, q) : rb;
                 thr = rb > thr ? rb : thr;
+                publish(rb, rq);
             }
             const float ts = thr_score(thr);
             bool maybe = false;
