@@ -282,7 +282,8 @@ __global__ __launch_bounds__(NTHR) void beam_decode_attn_kernel(const DecodePara
                     if constexpr (OUT_BF16) {
                         *(u32x2*)((uint16_t*)p.out + qoff + d) = u32x2{pack_bf16x2(r0, r1), pack_bf16x2(r2, r3)};
                     } else {
-                        *(f32x4*)((float*)p.out + qoff + d) = f32x4{r0, r1, r2, r3};
+                        // never re-read: non-temporal
+                        __builtin_nontemporal_store(f32x4{r0, r1, r2, r3}, (f32x4*)((float*)p.out + qoff + d));
                     }
                 }
         }

@@ -511,7 +511,7 @@ struct PersistentTask {
                                             pass * E::PCOLS * E::OB + c16 * 16)
                                     : 0x7FFFFFF0;
                 wait_lgkm0();
-                __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, off, 0, 2);   // nt: never re-read
             }
         }
     }

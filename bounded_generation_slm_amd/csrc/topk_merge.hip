@@ -461,6 +461,8 @@ __device__ __forceinline__ uint64_t round_bound(const float (&sc)[kWPerLane], co
     return ((uint64_t)tv << 32) - 1ull;
 }
 
+// The log-probs are read once: the stream's loads carry the non-temporal
+// policy (measured faster than cached loads on this path).
 // Vector-memory operations of the streaming loop are issued directly, so
 // that the compiler neither tracks nor waits for them: each round waits for
 // exactly its own loads (four rounds stay in flight), where compiler-placed
@@ -468,7 +470,7 @@ __device__ __forceinline__ uint64_t round_bound(const float (&sc)[kWPerLane], co
 // they fill are pinned after the wait that covers them.
 __device__ __forceinline__ f32x4 stream_load16(const float* p) {
     f32x4 r;
-    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+    asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(r) : "v"(p) : "memory");
     return r;
 }
 __device__ __forceinline__ float stream_load4(const float* p) {
