@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the timed oracle sample")
+    ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph timing of the step")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the reporting-only prefill-request and long-prompt beam timings")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -353,6 +354,31 @@ def main():
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
 
+    # the same step captured as one HIP graph (no per-launch host work)
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step([])
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step([])
+        for _ in range(max(1, args.warmup)):
+            g.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        ctx.check()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+
     per = {}
     for name, a, b in marks:
         per.setdefault(name, []).append(a.elapsed_time(b) * 1e3)   # us
@@ -407,6 +433,10 @@ def main():
             "gather_us": round(gather_us, 2),
         }, **beam.summary(per), host_wall_s=round(t_wall, 3)),
     }
+    if graph_ms is not None:
+        line["graph_replay"] = {"ms_per_step": round(graph_ms, 4),
+                                "tokens_per_s": round(pf.total_tokens / (graph_ms * 1e-3), 1),
+                                "what": "the same step captured once as a HIP graph and replayed"}
     line.update(extra)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pf, bs)

@@ -305,8 +305,14 @@ hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
     if (blocks == 0) return hipSuccess;
     const size_t lds = DecodeLds<D>::bytes(p.prompt_len);
     auto kern = beam_decode_attn_kernel<D, OUT_BF16, NTHR>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+    // raise the kernel's dynamic-LDS limit only when a call needs more than
+    // before (no host call per launch, so launches can be graph-captured)
+    static size_t lds_limit = 0;
+    if (lds > lds_limit) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        lds_limit = lds;
+    }
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NTHR), lds, stream, p, chunks, chunk_rows);
     return hipGetLastError();
 }
