@@ -19,6 +19,7 @@ typedef __attribute__((address_space(1))) void glb_void;
 
 constexpr int kKT = 32;                 // keys per K/V tile
 constexpr int kStages = 3;              // LDS ring depth (two tiles in flight)
+constexpr float kMaxLag = 8.f;          // how far (log2 units) the softmax reference max may trail
 
 // s_waitcnt with only a vmcnt limit (expcnt and lgkmcnt left at "no wait")
 template <int N>
@@ -147,14 +148,14 @@ __device__ __forceinline__ void issue_tile(char* ring, const LaneConst<D>& lc, c
 // One 32-key tile: S^T = K Q^T, online softmax (running max m in raw score
 // units, scale folded into exp2), O^T += V^T P^T.  The tile sits at LDS
 // address tbase + STAGE * STAGEB (relative to the lane constants' base).  When
-// MASK and apply, key kk of the tile (0..31) is left out where masked(kk).
+// MASK and apply, key kk of the tile (0..31) is left out where kk > lim (the
+// causal limit of the lane's query row, relative to the tile's first key).
 // The first tile a row sees must hold one of its keys (its running max then
 // becomes finite).
-template <int D, int STAGE, bool MASK, class Masked>
+template <int D, int STAGE, bool MASK>
 __device__ __forceinline__ void attend_tile(const LaneConst<D>& lc, uint32_t tbase,
                                             const u32x4 (&qreg)[Geo<D>::NKS], int hf, float c, float& m,
-                                            float& lsum, f32x16 (&o)[Geo<D>::NDB], bool apply,
-                                            const Masked& masked) {
+                                            float& lsum, f32x16 (&o)[Geo<D>::NDB], bool apply, int lim) {
     using G = Geo<D>;
     constexpr int H = G::NKS / 2;
     f32x16 sacc;
@@ -181,17 +182,23 @@ __device__ __forceinline__ void attend_tile(const LaneConst<D>& lc, uint32_t tba
         vop[db][0] = lds_read_tr16<STAGE * G::STAGEB>(lc.voff[db] + tbase);
         vop[db][1] = lds_read_tr16<STAGE * G::STAGEB + 8 * G::ROWB>(lc.voff[db] + tbase);
     }
-    if (MASK && apply) {                        // masked(key index in the tile) -> excluded
+    if (MASK && apply) {                        // element i holds key 8 (i / 4) + 4 hf + i % 4
+        const int lh = lim - 4 * hf;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            if (masked(8 * (i >> 2) + 4 * hf + (i & 3))) sacc[i] = -INFINITY;
+            if (8 * (i >> 2) + (i & 3) > lh) sacc[i] = -INFINITY;
     }
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[i]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    // The reference max m may trail the true running max by up to kMaxLag in
+    // exponent units: every weight exp2((s - m) c) then stays below 2^kMaxLag,
+    // and O and the row sum carry one common factor that the final division
+    // removes.  So O is rescaled only when some row's max moved further than
+    // that, which after the first tile is rare.
     const float mnew = fmaxf(m, tmax);          // finite: key 0 is in tile 0 for every row
-    if (__ballot(mnew > m) != 0) {              // rescale only when some running max moved
+    if (__ballot((mnew - m) * c > kMaxLag) != 0) {   // m = -inf on the first tile: always taken
         const float alpha = fast_exp2((m - mnew) * c);
         lsum *= alpha;
 #pragma unroll

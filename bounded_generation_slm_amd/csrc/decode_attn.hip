@@ -19,6 +19,7 @@
 // keys with vector dot products.  The workgroup also writes the suffix in the
 // current beam order (parent's history rows + the new row), so the reorder
 // after the previous merge costs no separate pass.
+#include <mutex>
 #include "common.h"
 #include "kernels.h"
 
@@ -306,12 +307,17 @@ hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
     const size_t lds = DecodeLds<D>::bytes(p.prompt_len);
     auto kern = beam_decode_attn_kernel<D, OUT_BF16, NTHR>;
     // raise the kernel's dynamic-LDS limit only when a call needs more than
-    // before (no host call per launch, so launches can be graph-captured)
+    // before (no host call per launch, so launches can be graph-captured);
+    // the lock keeps the recorded limit and the attribute in step across threads
+    static std::mutex lds_mu;
     static size_t lds_limit = 0;
-    if (lds > lds_limit) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        lds_limit = lds;
+    {
+        std::lock_guard<std::mutex> lock(lds_mu);
+        if (lds > lds_limit) {
+            hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            lds_limit = lds;
+        }
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NTHR), lds, stream, p, chunks, chunk_rows);
     return hipGetLastError();

@@ -155,11 +155,10 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(const PrefillParam
         issue_tile<D, (stage + 2) % kStages>(ring, lc, kbase, vbase, kv_stride, (t + 2) * kKT, L, wave);
         if (t > last_tile) return;              // whole tile above this wave's diagonal
         const int k0 = t * kKT;
-        const auto causal = [&](int kk) { return k0 + kk > qrow; };
         if (k0 + kKT - 1 > wrow0)
-            attend_tile<D, stage, true>(lc, 0u, qreg, hf, c, m, lsum, o, true, causal);
+            attend_tile<D, stage, true>(lc, 0u, qreg, hf, c, m, lsum, o, true, qrow - k0);
         else
-            attend_tile<D, stage, false>(lc, 0u, qreg, hf, c, m, lsum, o, false, causal);
+            attend_tile<D, stage, false>(lc, 0u, qreg, hf, c, m, lsum, o, false, 0);
     };
     issue_tile<D, 0>(ring, lc, kbase, vbase, kv_stride, 0, L, wave);
     issue_tile<D, 1>(ring, lc, kbase, vbase, kv_stride, kKT, L, wave);   // past the end it re-reads valid rows
@@ -537,9 +536,7 @@ struct PersistentTask {
         const int k0 = tc * kKT;
         if (tc <= last_tile) {
             // one body for both cases (two inlined copies would double the live registers)
-            const int qr = qrow;
-            attend_tile<D, STAGE, true>(lc, 0u, qreg, hf, c, m, lsum, o, k0 + kKT - 1 > wrow0,
-                                        [k0, qr](int kk) { return k0 + kk > qr; });
+            attend_tile<D, STAGE, true>(lc, 0u, qreg, hf, c, m, lsum, o, k0 + kKT - 1 > wrow0, qrow - k0);
         }
         end2 = end1;
         end1 = 0;
