@@ -52,9 +52,11 @@ def _load():
         lib.orc_gather_last.argtypes = [P, P, i32, i32, P]
         lib.orc_beam_decode_attn.argtypes = [i32] * 9 + [f64] + [P] * 11
         lib.orc_topk_merge.argtypes = [P, P, i32, i32, i32, i32, P, P, P]
+        lib.orc_topk_merge_logits.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P]
         lib.orc_reorder_suffix.argtypes = [i32] * 7 + [P] * 5
         for f in ("orc_prefill_attn", "orc_prefill_attn_rows", "orc_gather_last",
-                  "orc_beam_decode_attn", "orc_topk_merge", "orc_reorder_suffix"):
+                  "orc_beam_decode_attn", "orc_topk_merge", "orc_topk_merge_logits",
+                  "orc_reorder_suffix"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -151,6 +153,24 @@ def topk_merge(logprobs, cum, width):
     _check(_load().orc_topk_merge(_p(lp), _p(cm), R, Win, V, W, _p(tok), _p(par), _p(co)),
            "topk_merge")
     return tok, par, co
+
+
+def topk_merge_logits(logits, cum, width):
+    """logits [R,Win,V] fp32, cum [R,Win] fp32 -> (tokens, parent, score, lse):
+    tokens/parent [R,W] int32, score [R,W] fp64 (cum + logit - lse), lse
+    [R,Win] fp64 (each row's log-sum-exp).  The merge with the log-softmax of
+    each beam row folded in, all in fp64."""
+    x = _c(logits, np.float32)
+    cm = _c(cum, np.float32)
+    R, Win, V = x.shape
+    W = int(width)
+    tok = np.empty((R, W), np.int32)
+    par = np.empty((R, W), np.int32)
+    sc = np.empty((R, W), np.float64)
+    lse = np.empty((R, Win), np.float64)
+    _check(_load().orc_topk_merge_logits(_p(x), _p(cm), R, Win, V, W, _p(tok), _p(par), _p(sc), _p(lse)),
+           "topk_merge_logits")
+    return tok, par, sc, lse
 
 
 def reorder_suffix(parent, k_in, v_in, rows):

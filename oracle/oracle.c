@@ -13,7 +13,10 @@
  *   - beam search: all beams of a request share one prompt K/V and keep their
  *     own short suffix K/V (§1.2); each step merges per-beam candidates with
  *     the cumulative scores and keeps a fixed number, carrying parent indices
- *     (§1.1).
+ *     (§1.1);
+ *   - the same merge taking each beam row's logits, with the row's
+ *     log-softmax folded in (the next step the page's fixed beam-search
+ *     node runs on the model's output, §1.1).
  * Where the page is silent the readings are: GQA query head h reads KV head
  * floor(h*Hkv/Hq); softmax scale is a parameter (1/sqrt(D) in every workload);
  * the causal boundary includes the diagonal; candidate score is one IEEE fp32
@@ -260,6 +263,75 @@ int orc_topk_merge(const float *lp, const float *cum, int R, int Win, int V,
             tokens[(int64_t)r * W + j] = (int32_t)(best_f[j] % V);
             parent[(int64_t)r * W + j] = (int32_t)(best_f[j] / V);
             cum_out[(int64_t)r * W + j] = best_s[j];
+        }
+        free(best_s);
+        free(best_f);
+    }
+    return 0;
+}
+
+/* Beam top-k merge on logits (the merge with its log-softmax folded in).
+ * For request r and beam row b: lse[r,b] = log sum_v exp(x[r,b,v]) over the
+ * row's V logits (fp64, shifted by the row maximum); the log-probability of
+ * (b,v) is x - lse and the candidate score is cum[r,b] + (x - lse), all in
+ * fp64.  Candidates rank by score descending, then flat index f = b*V + v
+ * ascending; the W first are written in that order (token = f mod V, parent
+ * = f div V, score), with every row's lse.  Logits are finite or -inf, and
+ * every row holds at least one finite logit. */
+int orc_topk_merge_logits(const float *x, const float *cum, int R, int Win, int V,
+                          int W, int32_t *tokens, int32_t *parent, double *score_out,
+                          double *lse_out)
+{
+    if (R <= 0 || Win <= 0 || V <= 0 || W <= 0 || (int64_t)W > (int64_t)Win * V)
+        return 1;
+    int bad = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < (int64_t)R * Win; ++row) {
+        const float *xr = x + row * V;
+        double m = -INFINITY;
+        for (int v = 0; v < V; ++v)
+            if ((double)xr[v] > m)
+                m = xr[v];
+        double s = 0.0;
+        for (int v = 0; v < V; ++v)
+            s += exp((double)xr[v] - m);       /* exp(-inf) = 0 */
+        if (!(m > -INFINITY) || !isfinite(m) || isnan(s)) {
+#pragma omp atomic write
+            bad = 1;
+        }
+        lse_out[row] = m + log(s);
+    }
+    if (bad)
+        return 1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < R; ++r) {
+        double *best_s = malloc(sizeof(double) * (size_t)W);
+        int64_t *best_f = malloc(sizeof(int64_t) * (size_t)W);
+        int count = 0;
+        for (int b = 0; b < Win; ++b) {
+            const int64_t row = (int64_t)r * Win + b;
+            const double c = cum[row], lse = lse_out[row];
+            for (int v = 0; v < V; ++v) {
+                const double s = c + ((double)x[row * V + v] - lse);
+                const int64_t f = (int64_t)b * V + v;
+                if (count == W && !(s > best_s[W - 1] || (s == best_s[W - 1] && f < best_f[W - 1])))
+                    continue;
+                int pos = count < W ? count : W - 1;
+                if (count < W)
+                    ++count;
+                while (pos > 0 && (s > best_s[pos - 1] || (s == best_s[pos - 1] && f < best_f[pos - 1]))) {
+                    best_s[pos] = best_s[pos - 1];
+                    best_f[pos] = best_f[pos - 1];
+                    --pos;
+                }
+                best_s[pos] = s;
+                best_f[pos] = f;
+            }
+        }
+        for (int j = 0; j < W; ++j) {
+            tokens[(int64_t)r * W + j] = (int32_t)(best_f[j] % V);
+            parent[(int64_t)r * W + j] = (int32_t)(best_f[j] / V);
+            score_out[(int64_t)r * W + j] = best_s[j];
         }
         free(best_s);
         free(best_f);
