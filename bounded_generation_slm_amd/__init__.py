@@ -37,7 +37,8 @@ SLM_BF16, SLM_F32 = 0, 1
 EXPORTED = (
     "slm_abi_version", "slm_status_string", "slm_ctx_create", "slm_ctx_destroy",
     "slm_ctx_set_stream", "slm_ctx_check", "slm_ctx_last_error", "slm_packed_prefill_attn",
-    "slm_gather_last", "slm_beam_decode_attn", "slm_beam_topk_merge", "slm_beam_reorder_suffix",
+    "slm_gather_last", "slm_beam_decode_attn", "slm_beam_topk_merge", "slm_beam_topk_merge_logits",
+    "slm_beam_reorder_suffix",
 )
 
 
@@ -71,9 +72,11 @@ _lib.slm_packed_prefill_attn.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
 _lib.slm_gather_last.argtypes = [_P, _P, _P, _I, _I, _I, ctypes.c_int, _P]
 _lib.slm_beam_decode_attn.argtypes = [_P, ctypes.POINTER(_BeamAttnArgs)]
 _lib.slm_beam_topk_merge.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]
+_lib.slm_beam_topk_merge_logits.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P]
 _lib.slm_beam_reorder_suffix.argtypes = [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
 for _name in ("slm_ctx_create", "slm_ctx_set_stream", "slm_ctx_check", "slm_packed_prefill_attn",
-              "slm_gather_last", "slm_beam_decode_attn", "slm_beam_topk_merge", "slm_beam_reorder_suffix"):
+              "slm_gather_last", "slm_beam_decode_attn", "slm_beam_topk_merge", "slm_beam_topk_merge_logits",
+              "slm_beam_reorder_suffix"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -170,6 +173,10 @@ class Context:
 
     def beam_topk_merge(self, logprobs, cum, width: int, tokens=None, parent=None, cum_out=None):
         return slm_beam_topk_merge(self, logprobs, cum, width, tokens, parent, cum_out)
+
+    def beam_topk_merge_logits(self, logits, cum, width: int, tokens=None, parent=None, cum_out=None,
+                               lse_out=None):
+        return slm_beam_topk_merge_logits(self, logits, cum, width, tokens, parent, cum_out, lse_out)
 
     def beam_reorder_suffix(self, parent, k_in, v_in, rows: int, k_out, v_out):
         return slm_beam_reorder_suffix(self, parent, k_in, v_in, rows, k_out, v_out)
@@ -281,6 +288,33 @@ def slm_beam_topk_merge(ctx: Context, logprobs, cum, width: int, tokens=None, pa
         R, Win, V, W, _ptr(tokens, "tokens", (torch.int32,), dev), _ptr(parent, "parent", (torch.int32,), dev),
         _ptr(cum_out, "cum_out", (torch.float32,), dev))
     ctx._raise(rc, "slm_beam_topk_merge")
+    return tokens, parent, cum_out
+
+
+def slm_beam_topk_merge_logits(ctx: Context, logits, cum, width: int, tokens=None, parent=None, cum_out=None,
+                               lse_out=None):
+    """logits [R,Win,V] fp32, cum [R,Win] fp32 -> (tokens, parent, cum_out) [R,W]; lse_out [R,Win]
+    fp32 (optional) receives each row's log-sum-exp."""
+    dev = ctx.device
+    R, Win, V = logits.shape
+    if tuple(cum.shape) != (R, Win):
+        raise ValueError("cum must be [R, Win]")
+    if lse_out is not None and tuple(lse_out.shape) != (R, Win):
+        raise ValueError("lse_out must be [R, Win]")
+    W = int(width)
+    tokens = torch.empty((R, W), dtype=torch.int32, device=dev) if tokens is None else tokens
+    parent = torch.empty((R, W), dtype=torch.int32, device=dev) if parent is None else parent
+    cum_out = torch.empty((R, W), dtype=torch.float32, device=dev) if cum_out is None else cum_out
+    for name, t in (("tokens", tokens), ("parent", parent), ("cum_out", cum_out)):
+        if tuple(t.shape) != (R, W):
+            raise ValueError("%s must be [R, W]" % name)
+    ctx._stream()
+    rc = _lib.slm_beam_topk_merge_logits(
+        ctx._h, _ptr(logits, "logits", (torch.float32,), dev), _ptr(cum, "cum", (torch.float32,), dev),
+        R, Win, V, W, _ptr(tokens, "tokens", (torch.int32,), dev), _ptr(parent, "parent", (torch.int32,), dev),
+        _ptr(cum_out, "cum_out", (torch.float32,), dev),
+        None if lse_out is None else _ptr(lse_out, "lse_out", (torch.float32,), dev))
+    ctx._raise(rc, "slm_beam_topk_merge_logits")
     return tokens, parent, cum_out
 
 

@@ -11,6 +11,7 @@ enum DeviceError : int {
     kErrNone = 0,
     kErrCuSeqlens = 1,     // cu_seqlens not monotone / out of [0,T] / length > max_seqlen
     kErrParent = 2,        // parent index outside [0, W)
+    kErrSelect = 3,        // a top-k selection did not converge (equal keys: never for valid inputs)
 };
 
 
@@ -98,9 +99,23 @@ struct TopkParams {
     int64_t list_cap;                   // keys per request list
     int64_t seg;                        // candidates per stage-1 wave (a multiple of 4)
     int num_requests, beams_in, vocab, width;
+    // merge on logits only (logprobs then holds the logits):
+    float2* parts;                      // workspace: per (stage-1 wave, row it touches) (max, sum of exp)
+    float* lse_out;                     // [R, Win] each row's log-sum-exp, or null
+    int rpw;                            // part slots per stage-1 wave: rows one wave can touch
+    int* err;                           // device error flag
 };
 hipError_t launch_beam_topk_merge(const TopkParams& p, hipStream_t stream);
+hipError_t launch_beam_topk_merge_logits(const TopkParams& p, hipStream_t stream);
 size_t beam_topk_workspace_bytes(int max_requests, int max_beams);
+int64_t beam_topk_lists(int max_beams);         // list slots (of up to max_beams keys) per request
+int64_t beam_topk_parts_cap(int max_requests, int max_beams);
+// candidates per stage-1 wave of the merge on logits: as beam_topk_segment, with
+// every piece (one row's part of one range) taking a list slot, and the waves'
+// part slots within parts_cap; sets rpw
+int64_t beam_topk_logits_segment(int num_requests, int beams_in, int vocab, int64_t resident_waves, int64_t lists,
+                                 int64_t parts_cap, int& rpw);
+int beam_topk_logits_blocks_per_cu(int width);
 // candidates per stage-1 wave: the call split evenly over the resident waves,
 // at least kTopkMinSegment, and few enough ranges per request for its list
 // (`lists` slots of W keys)

@@ -33,6 +33,7 @@ struct slm_ctx {
     int num_cus = 256;
     size_t max_lds = 0;
     int topk_blocks_per_cu[slm::kTopkMaxWidth + 1] = {0};   // stage-1 occupancy per width (0 = not queried)
+    int topk_logits_blocks_per_cu[slm::kTopkMaxWidth + 1] = {0};   // the same, merge on logits
     char last_error[512] = {0};
 };
 
@@ -151,7 +152,7 @@ slm_status slm_ctx_create(int device, const slm_caps* caps, slm_ctx** out) {
     }
     ctx->plan_cap = (int)entries;
     ctx->topk_ws_bytes = slm::beam_topk_workspace_bytes(c.max_requests, c.max_beams);
-    ctx->topk_lists = std::max<int64_t>((int64_t)c.max_beams, slm::kTopkMaxChunks);
+    ctx->topk_lists = slm::beam_topk_lists(c.max_beams);
     if (hipMalloc((void**)&ctx->topk_ws, ctx->topk_ws_bytes) != hipSuccess ||
         hipMemset(ctx->topk_ws, 0, ctx->topk_ws_bytes) != hipSuccess ||
         hipMalloc((void**)&ctx->err_flag, sizeof(int)) != hipSuccess ||
@@ -198,6 +199,8 @@ slm_status slm_ctx_check(slm_ctx* ctx) {
         (void)hipMemset(ctx->err_flag, 0, sizeof(int));
         if (flag == slm::kErrCuSeqlens)
             return fail(ctx, SLM_ERR_INVALID_ARG, "cu_seqlens: not non-decreasing in [0,T] or a length above max_seqlen");
+        if (flag == slm::kErrSelect)
+            return fail(ctx, SLM_ERR_DEVICE, "top-k: a selection pass limit was reached (equal keys)");
         return fail(ctx, SLM_ERR_INVALID_ARG, "parent index outside [0, width)");
     }
     return ok(ctx);
@@ -374,6 +377,7 @@ slm_status slm_beam_topk_merge(slm_ctx* ctx, const float* logprobs, const float*
         return fail(ctx, SLM_ERR_ALIAS, "topk: outputs overlap each other");
     slm::TopkParams p{};
     p.logprobs = logprobs; p.cum = cum; p.tokens = tokens; p.parent = parent; p.cum_out = cum_out;
+    p.err = ctx->err_flag;
     const int64_t R_cap = ctx->caps.max_requests;
     p.req_state = ctx->topk_ws;
     p.stage1 = ctx->topk_ws + slm::kTopkStateWords * R_cap;
@@ -386,6 +390,61 @@ slm_status slm_beam_topk_merge(slm_ctx* ctx, const float* logprobs, const float*
     const int64_t resident = (int64_t)ctx->num_cus * bpc * 4;
     p.seg = slm::beam_topk_segment(num_requests, beams_in, vocab, resident, ctx->topk_lists);
     return SLM_LAUNCH(ctx, slm::launch_beam_topk_merge(p, ctx->stream), "topk");
+}
+
+slm_status slm_beam_topk_merge_logits(slm_ctx* ctx, const float* logits, const float* cum, int32_t num_requests,
+                                      int32_t beams_in, int32_t vocab, int32_t width, int32_t* tokens,
+                                      int32_t* parent, float* cum_out, float* lse_out) {
+    slm_status s = enter(ctx);
+    if (s != SLM_OK) return s;
+    if (num_requests < 0 || beams_in <= 0 || vocab <= 0 || width <= 0)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "topk_logits: a size is out of range");
+    if ((int64_t)width > (int64_t)beams_in * vocab)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "topk_logits: width %d > beams_in * vocab", width);
+    if ((int64_t)beams_in * vocab >= ((int64_t)1 << 31))
+        return fail(ctx, SLM_ERR_UNSUPPORTED, "topk_logits: beams_in * vocab must be below 2^31");
+    if (width > slm::kTopkMaxWidth || beams_in > slm::kTopkMaxWidth)
+        return fail(ctx, SLM_ERR_UNSUPPORTED, "topk_logits: width and beams_in must be at most %d", slm::kTopkMaxWidth);
+    if (num_requests > ctx->caps.max_requests || beams_in > ctx->caps.max_beams || width > ctx->caps.max_beams ||
+        vocab > ctx->caps.max_vocab)
+        return fail(ctx, SLM_ERR_CAPACITY, "topk_logits: beyond the context caps (requests %d, beams %d, vocab %d)",
+                    ctx->caps.max_requests, ctx->caps.max_beams, ctx->caps.max_vocab);
+    if (num_requests == 0) return ok(ctx);
+    if (!logits || !cum || !tokens || !parent || !cum_out)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "topk_logits: NULL tensor");
+    if (((uintptr_t)logits & 3) || ((uintptr_t)cum & 3) || ((uintptr_t)tokens & 3) || ((uintptr_t)parent & 3) ||
+        ((uintptr_t)cum_out & 3) || ((uintptr_t)lse_out & 3))
+        return fail(ctx, SLM_ERR_INVALID_ARG, "topk_logits: tensors must be 4-byte aligned");
+    const size_t R = num_requests;
+    const size_t xb = R * beams_in * (size_t)vocab * 4, cb = R * beams_in * 4, ob = R * width * 4;
+    const void* outs[] = {tokens, parent, cum_out};
+    for (const void* o : outs)
+        if (overlaps(o, ob, logits, xb) || overlaps(o, ob, cum, cb))
+            return fail(ctx, SLM_ERR_ALIAS, "topk_logits: an output overlaps an input");
+    if (overlaps(tokens, ob, parent, ob) || overlaps(tokens, ob, cum_out, ob) || overlaps(parent, ob, cum_out, ob))
+        return fail(ctx, SLM_ERR_ALIAS, "topk_logits: outputs overlap each other");
+    if (lse_out) {
+        if (overlaps(lse_out, cb, logits, xb) || overlaps(lse_out, cb, cum, cb))
+            return fail(ctx, SLM_ERR_ALIAS, "topk_logits: lse_out overlaps an input");
+        for (const void* o : outs)
+            if (overlaps(lse_out, cb, o, ob)) return fail(ctx, SLM_ERR_ALIAS, "topk_logits: lse_out overlaps an output");
+    }
+    slm::TopkParams p{};
+    p.logprobs = logits; p.cum = cum; p.tokens = tokens; p.parent = parent; p.cum_out = cum_out;
+    p.lse_out = lse_out;
+    p.err = ctx->err_flag;
+    const int64_t R_cap = ctx->caps.max_requests;
+    p.req_state = ctx->topk_ws;
+    p.stage1 = ctx->topk_ws + slm::kTopkStateWords * R_cap;
+    p.list_cap = ctx->topk_lists * ctx->caps.max_beams;
+    p.parts = (float2*)(p.stage1 + R_cap * p.list_cap);
+    p.num_requests = num_requests; p.beams_in = beams_in; p.vocab = vocab; p.width = width;
+    int& bpc = ctx->topk_logits_blocks_per_cu[width];
+    if (bpc == 0) bpc = ctx->dry_run ? 1 : slm::beam_topk_logits_blocks_per_cu(width);
+    const int64_t resident = (int64_t)ctx->num_cus * bpc * 4;
+    p.seg = slm::beam_topk_logits_segment(num_requests, beams_in, vocab, resident, ctx->topk_lists,
+                                          slm::beam_topk_parts_cap(ctx->caps.max_requests, ctx->caps.max_beams), p.rpw);
+    return SLM_LAUNCH(ctx, slm::launch_beam_topk_merge_logits(p, ctx->stream), "topk_logits");
 }
 
 slm_status slm_beam_reorder_suffix(slm_ctx* ctx, int32_t n_layers, int32_t num_requests, int32_t width,

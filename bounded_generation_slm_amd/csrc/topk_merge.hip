@@ -129,15 +129,22 @@ __device__ void block_minmax(SelectorLds& s, int cnt, uint64_t lo, uint64_t hi, 
 // keys still in play, so concentrated keys (log-probs share their sign and
 // exponent bits) still spread over the bins instead of piling into one; one
 // pass usually leaves a handful of keys.
-__device__ uint64_t select_kth(SelectorLds& s, int cnt, int k) {
+// Each pass narrows [lo, hi] to one bin, at least 11 bits fewer, so distinct
+// keys finish within 7 passes; kSelectPasses bounds the loop regardless.
+constexpr int kSelectPasses = 16;
+__device__ uint64_t select_kth(SelectorLds& s, int cnt, int k, int* err) {
     const int tid = threadIdx.x;
     uint64_t lo = 0ull, hi = ~0ull;
     int c = cnt;                                    // keys in [lo, hi]
-    for (;;) {
+    for (int pass = 0;; ++pass) {
         uint64_t mn, mx;
         block_minmax(s, cnt, lo, hi, mn, mx);
         if (k == 1) return mx;
         if (k == c) return mn;
+        if (pass == kSelectPasses || mn == mx) {   // equal keys: not a valid input
+            if (tid == 0) raise_error(err, kErrSelect);
+            return mn;
+        }
         lo = mn;
         hi = mx;                                    // c >= 2 distinct keys: mn < mx
         const int bits = 64 - __clzll(hi - lo);
@@ -181,15 +188,18 @@ __device__ uint64_t select_kth(SelectorLds& s, int cnt, int k) {
 }
 
 // Keep exactly the W largest keys in s.buf[0..W); raise the threshold.
-__device__ void compact(SelectorLds& s, int width) {
+__device__ void compact(SelectorLds& s, int width, int* err) {
     const int cnt = s.cnt;
     if (cnt <= width) return;                       // uniform: read after a barrier
-    const uint64_t kth = select_kth(s, cnt, width);
+    const uint64_t kth = select_kth(s, cnt, width, err);
     if (threadIdx.x == 0) s.spos = 0;
     __syncthreads();
     for (int i = threadIdx.x; i < cnt; i += kTkThreads) {
         const uint64_t key = s.buf[i];
-        if (key >= kth) s.surv[atomicAdd(&s.spos, 1)] = key;
+        if (key >= kth) {
+            const int pos = atomicAdd(&s.spos, 1);
+            if (pos < width) s.surv[pos] = key;     // exactly width for distinct keys
+        }
     }
     __syncthreads();
     for (int i = threadIdx.x; i < width; i += kTkThreads) s.buf[i] = s.surv[i];
@@ -334,10 +344,10 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 
 // k-th largest (1-based) of buf[0..cnt), wave-level radix select over the
 // live [min, max] range (see select_kth).
-__device__ uint64_t wave_select_kth(const uint64_t* buf, int* hist, int cnt, int k, int lane) {
+__device__ uint64_t wave_select_kth(const uint64_t* buf, int* hist, int cnt, int k, int lane, int* err) {
     uint64_t lo = 0ull, hi = ~0ull;
     int c = cnt;
-    for (;;) {
+    for (int pass = 0;; ++pass) {
         uint64_t a = ~0ull, b = 0ull;
         for (int i = lane; i < cnt; i += kWLanes) {
             const uint64_t key = buf[i];
@@ -349,6 +359,10 @@ __device__ uint64_t wave_select_kth(const uint64_t* buf, int* hist, int cnt, int
         const uint64_t mn = wave_umin64(a), mx = wave_umax64(b);
         if (k == 1) return mx;
         if (k == c) return mn;
+        if (pass == kSelectPasses || mn == mx) {   // equal keys: not a valid input (8 bits a pass: 8 passes)
+            if (lane == 0) raise_error(err, kErrSelect);
+            return mn;
+        }
         lo = mn;
         hi = mx;
         const int bits = 64 - __clzll(hi - lo);
@@ -393,15 +407,15 @@ __device__ uint64_t wave_select_kth(const uint64_t* buf, int* hist, int cnt, int
 
 // Keep exactly the W largest keys of buf[0..cnt) in buf[0..W).  Returns the
 // W-th key (the new threshold); cnt becomes W.
-__device__ uint64_t wave_compact(uint64_t* buf, uint64_t* surv, int* hist, int& cnt, int W, int lane) {
-    const uint64_t kth = wave_select_kth(buf, hist, cnt, W, lane);
+__device__ uint64_t wave_compact(uint64_t* buf, uint64_t* surv, int* hist, int& cnt, int W, int lane, int* err) {
+    const uint64_t kth = wave_select_kth(buf, hist, cnt, W, lane, err);
     int pos = 0;
     for (int i0 = 0; i0 < cnt; i0 += kWLanes) {
         const int i = i0 + lane;
         const uint64_t key = i < cnt ? buf[i] : 0ull;
         const bool keep = i < cnt && key >= kth;
         const uint64_t m = __ballot(keep);
-        if (keep) surv[pos + lanes_below(m)] = key;
+        if (keep && pos + lanes_below(m) < W) surv[pos + lanes_below(m)] = key;   // exactly W for distinct keys
         pos += __popcll(m);
     }
     wave_fence();
@@ -461,38 +475,14 @@ __device__ __forceinline__ uint64_t round_bound(const float (&sc)[kWPerLane], co
     return ((uint64_t)tv << 32) - 1ull;
 }
 
-// The log-probs are read once: the stream's loads carry the non-temporal
-// policy (measured faster than cached loads on this path).
-// Vector-memory operations of the streaming loop are issued directly, so
-// that the compiler neither tracks nor waits for them: each round waits for
-// exactly its own loads (four rounds stay in flight), where compiler-placed
-// waits merged over the rare insertion path drain the pipeline.  Registers
-// they fill are pinned after the wait that covers them.
+// The log-probs (logits) are read once: the stream's loads carry the
+// non-temporal policy (measured faster than cached loads on this path).  All
+// loads are ordinary compiler-visible loads, so the compiler tracks their
+// destination registers and places the waits.
 __device__ __forceinline__ f32x4 stream_load16(const float* p) {
-    f32x4 r;
-    asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(r) : "v"(p) : "memory");
-    return r;
+    return __builtin_nontemporal_load((const f32x4*)p);
 }
-__device__ __forceinline__ float stream_load4(const float* p) {
-    float r;
-    asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(p) : "memory");
-    return r;
-}
-// agent-coherent 8-byte load (the shared bounds are written by atomics of other CUs)
-__device__ __forceinline__ uint64_t coherent_load8(const uint64_t* p) {
-    uint64_t r;
-    asm volatile("global_load_dwordx2 %0, %1, off sc1" : "=v"(r) : "v"(p) : "memory");
-    return r;
-}
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-template <class T>
-__device__ __forceinline__ void pin(T& x) {
-    asm volatile("" : "+v"(x));
-}
+__device__ __forceinline__ float stream_load4(const float* p) { return __builtin_nontemporal_load(p); }
 
 template <bool VEC>
 __global__ __launch_bounds__(kTkThreads) void topk_stage1_kernel(const TopkParams p) {
@@ -521,9 +511,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage1_kernel(const TopkParam
 
     // Publish a W-th-key bound to word 0 and a q-th-key bound to this wave's
     // slot (each backed by that many of this wave's candidates at or above
-    // it).  The atomics return nothing; in the stream's waits, which count
-    // only loads issued after the awaited ones (and loads return in order),
-    // they can only make a wait stricter.
+    // it).  The atomics return nothing.
     auto publish = [&](uint64_t own, uint64_t oq) {
         if (own > pub && lane == 0) atomicMax((unsigned long long*)req_thr(p, r), (unsigned long long)own);
         if (oq > pubq && lane == 0) atomicMax((unsigned long long*)req_slot(p, r, slot), (unsigned long long)oq);
@@ -534,9 +522,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage1_kernel(const TopkParam
     // and the q-th of them.
     auto shrink = [&]() {
         wave_fence();
-        const uint64_t own = wave_compact(buf, surv, hist, cnt, W, lane);
+        const uint64_t own = wave_compact(buf, surv, hist, cnt, W, lane, p.err);
         thr = own > thr ? own : thr;
-        const uint64_t oq = q < W ? wave_select_kth(buf, hist, W, q, lane) : own;
+        const uint64_t oq = q < W ? wave_select_kth(buf, hist, W, q, lane, p.err) : own;
         wave_fence();
         publish(own, oq);
     };
@@ -592,7 +580,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage1_kernel(const TopkParam
         const uint32_t f0 = (uint32_t)(a - (int64_t)r * req_len);   // flat index b*V + v of lp[0]
         const uint64_t* baddr = bound_addr(p, r, lane, m_slots);
         const int rounds = (n + kWRound - 1) / kWRound;
-        vm_wait<0>();                                           // nothing of earlier pieces stays in flight
         f32x4 B0[NV], B1[NV], B2[NV], B3[NV];
         // loads of round rd (clamped into the piece: rounds past its end
         // re-read valid addresses, and their values are never used)
@@ -609,8 +596,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage1_kernel(const TopkParam
             }
         };
         auto round = [&](int rd, f32x4 (&src)[NV]) {
-#pragma unroll
-            for (int j = 0; j < NV; ++j) pin(src[j]);
             float sc[kWPerLane];
 #pragma unroll
             for (int j = 0; j < NV; ++j)
@@ -647,35 +632,29 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage1_kernel(const TopkParam
                 }
             if (cnt > soft) shrink();
         };
-        // The shared bound is read once per group of four rounds, issued with
-        // the group's first loads and taken up at its last round.
-        // Issue order per group: F(rd+3) S F(rd+4) F(rd+5) F(rd+6); a round
-        // waits until only the operations issued after its own loads remain.
+        // Four rounds of loads stay in flight; the shared bound is read once
+        // per group of four rounds, issued with the group's first loads and
+        // taken up at its last round.
         fetch(0, B0);
         fetch(1, B1);
         fetch(2, B2);
+        uint64_t sh = 0;
         for (int rd = 0; rd < rounds; rd += kWDepth) {
             fetch(rd + 3, B3);
-            uint64_t sh = coherent_load8(baddr);
-            vm_wait<3 * LPF + 1>();
+            sh = load_relaxed(baddr);
             round(rd, B0);
             if (rd + 1 >= rounds) break;
             fetch(rd + 4, B0);
-            vm_wait<3 * LPF + 1>();
             round(rd + 1, B1);
             if (rd + 2 >= rounds) break;
             fetch(rd + 5, B1);
-            vm_wait<3 * LPF + 1>();
             round(rd + 2, B2);
             if (rd + 3 >= rounds) break;
             fetch(rd + 6, B2);
-            vm_wait<3 * LPF>();
-            pin(sh);
             const uint64_t u = bound_take(sh, lane, m_slots);
             thr = u > thr ? u : thr;
             round(rd + 3, B3);
         }
-        vm_wait<0>();                                           // loads issued past the piece's end land here
         a = pe;
     }
     flush();
@@ -704,9 +683,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage2_kernel(const TopkParam
         }
         insert(s, keys, thr);
         __syncthreads();
-        if (s.cnt > kSoftCap) compact(s, W);
+        if (s.cnt > kSoftCap) compact(s, W, p.err);
     }
-    compact(s, W);
+    compact(s, W, p.err);
     int S = 2;
     while (S < W) S <<= 1;
     sort_desc(s, min(s.cnt, W), S);
@@ -723,13 +702,249 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage2_kernel(const TopkParam
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
+
+// ---- the merge on logits: each beam row's log-softmax folded in ----
+//
+// The score of (b, v) is cum[b] + (x[b, v] - lse[b]) with lse[b] the
+// log-sum-exp of row b's logits, so within one row candidates rank by the
+// logit alone: a request's top W lie among the top W logits of each row,
+// and the top W of each piece (one row's part of one wave's range) contain
+// those.  Stage 1 streams the logits once, keeping per piece its W largest
+// logit keys (key = order(x) << 32 | ~f) and the piece's (max, sum of
+// exp(x - max)); stage 2 combines each row's pieces into its lse, re-keys
+// every kept candidate by its fp32 score fl(cum + fl(x - lse)) and selects
+// as the merge on log-probs does.  No bound is shared across rows: a
+// candidate's score needs its row's lse, known only once the row is done.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLogitFloor = -1e30f;              // running max before any finite logit
+
+__device__ __forceinline__ int64_t part_slot(int64_t wid, int64_t row, int64_t seg, int V, int rpw) {
+    return wid * rpw + (row - wid * seg / V);
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kTkThreads) void topk_logits_stage1_kernel(const TopkParams p) {
+    extern __shared__ __attribute__((aligned(16))) uint64_t wave_lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t wid = (int64_t)blockIdx.x * (kTkThreads / kWLanes) + wave;
+    const int V = p.vocab, W = p.width;
+    const int64_t req_len = (int64_t)p.beams_in * V;
+    const int64_t total = (int64_t)p.num_requests * req_len;
+    int64_t a = wid * p.seg;                                    // this wave's range [a, end)
+    if (a >= total) return;                                     // no barriers below: waves are independent
+    const int64_t end = min(total, a + p.seg);
+    uint64_t* buf = wave_lds + (size_t)wave * wave_lds_words(W);
+    const int soft = wave_soft_cap(W);
+    uint64_t* surv = buf + soft + kWRound;
+    int* hist = (int*)(surv + ((W + 1) & ~1));
+
+    constexpr int NV = kWPerLane / 4;
+    constexpr int LPF = VEC ? NV : kWPerLane;                   // load instructions per round
+    while (a < end) {
+        const int64_t row = a / V;                              // r * Win + b
+        const int r = (int)(row / p.beams_in);
+        const int64_t pe = min(end, (row + 1) * V);             // this piece: [a, pe) inside one row
+        const int n = (int)(pe - a);
+        const float* xp = p.logprobs + a;
+        const uint32_t f0 = (uint32_t)(a - (int64_t)r * req_len);   // flat index b*V + v of xp[0]
+        const int rounds = (n + kWRound - 1) / kWRound;
+        uint64_t thr = 0;                                       // keys > thr pass (this piece only)
+        int cnt = 0;
+        float lm = kLogitFloor, ls = 0.f;                       // lane's running max, sum of exp(x - lm)
+        auto shrink = [&]() {
+            wave_fence();
+            const uint64_t own = wave_compact(buf, surv, hist, cnt, W, lane, p.err);
+            thr = own > thr ? own : thr;
+            wave_fence();
+        };
+        f32x4 B0[NV], B1[NV], B2[NV], B3[NV];
+        auto fetch = [&](int rd, f32x4 (&dst)[NV]) {
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                const int i0 = rd * kWRound + (j * kWLanes + lane) * 4;
+                if (VEC) {
+                    dst[j] = stream_load16(xp + min(i0, n - 4));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dst[j][e] = stream_load4(xp + min(i0 + e, n - 1));
+                }
+            }
+        };
+        auto round = [&](int rd, f32x4 (&src)[NV]) {
+            float x[kWPerLane];
+            bool valid[kWPerLane];
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[j * 4 + e] = src[j][e];
+                    valid[j * 4 + e] = rd * kWRound + (j * kWLanes + lane) * 4 + e < n;
+                }
+            // the row's normaliser: clamped re-reads are logits of this piece
+            // too, so they may join the max but not the sum
+            float rmax = x[0];
+#pragma unroll
+            for (int k = 1; k < kWPerLane; ++k) rmax = fmaxf(rmax, x[k]);
+            if (rmax > lm) {
+                ls *= fast_exp2((lm - rmax) * kLog2e);
+                lm = rmax;
+            }
+            const float ml = lm * kLog2e;
+#pragma unroll
+            for (int k = 0; k < kWPerLane; ++k) {
+                const float e = fast_exp2(fmaf(x[k], kLog2e, -ml));
+                ls += valid[k] ? e : 0.f;
+            }
+            // candidates: the piece's W largest logits
+            if (rd == 0 && W <= kWRound / 2) {                  // a piece's first round: bound it at once
+                const uint64_t rb = round_bound(x, valid, W);
+                thr = rb > thr ? rb : thr;
+            }
+            const float ts = thr_score(thr);
+            bool maybe = false;
+#pragma unroll
+            for (int k = 0; k < kWPerLane; ++k) maybe |= x[k] >= ts;
+            if (__ballot(maybe) == 0) return;
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool ok = x[j * 4 + e] >= ts;
+                    if (__ballot(ok) == 0) continue;
+                    const int i = rd * kWRound + (j * kWLanes + lane) * 4 + e;
+                    const uint64_t key = (ok && i < n) ? make_key(x[j * 4 + e], f0 + (uint32_t)i) : 0ull;
+                    const bool pass = key > thr;
+                    const uint64_t m = __ballot(pass);
+                    if (pass) buf[cnt + lanes_below(m)] = key;
+                    cnt += __popcll(m);
+                }
+            if (cnt > soft) shrink();
+        };
+        fetch(0, B0);
+        fetch(1, B1);
+        fetch(2, B2);
+        for (int rd = 0; rd < rounds; rd += kWDepth) {
+            fetch(rd + 3, B3);
+            round(rd, B0);
+            if (rd + 1 >= rounds) break;
+            fetch(rd + 4, B0);
+            round(rd + 1, B1);
+            if (rd + 2 >= rounds) break;
+            fetch(rd + 5, B1);
+            round(rd + 2, B2);
+            if (rd + 3 >= rounds) break;
+            fetch(rd + 6, B2);
+            round(rd + 3, B3);
+        }
+        // the piece's (max, sum of exp(x - max)) over its lanes
+        float M = lm;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        float S = ls * fast_exp2((lm - M) * kLog2e);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off);
+        if (lane == 0) p.parts[part_slot(wid, row, p.seg, V, p.rpw)] = float2{M, S};
+        // the piece's W largest keys go to request r's list
+        wave_fence();
+        if (cnt > W) shrink();
+        int base = 0;
+        if (lane == 0 && cnt > 0) base = atomicAdd(req_cnt(p, r), cnt);
+        base = __shfl(base, 0);
+        uint64_t* list = p.stage1 + (int64_t)r * p.list_cap;
+        for (int i = lane; i < cnt; i += kWLanes) list[base + i] = buf[i];
+        wave_fence();
+        a = pe;
+    }
+}
+
+// Stage 2 of the merge on logits: per request, the rows' lse from their
+// pieces (in piece order), then the kept candidates re-keyed by score.
+__global__ __launch_bounds__(kTkThreads) void topk_logits_stage2_kernel(const TopkParams p) {
+    __shared__ SelectorLds s;
+    __shared__ float lse_s[kTopkMaxWidth];
+    const int r = blockIdx.x;
+    const int W = p.width, V = p.vocab, Win = p.beams_in;
+    for (int b = threadIdx.x; b < Win; b += kTkThreads) {
+        const int64_t row = (int64_t)r * Win + b;
+        const int64_t w0 = row * V / p.seg, w1 = (row * V + V - 1) / p.seg;
+        float M = kLogitFloor;
+        for (int64_t w = w0; w <= w1; ++w) M = fmaxf(M, p.parts[part_slot(w, row, p.seg, V, p.rpw)].x);
+        float S = 0.f;
+        for (int64_t w = w0; w <= w1; ++w) {
+            const float2 q = p.parts[part_slot(w, row, p.seg, V, p.rpw)];
+            S += q.y * fast_exp2((q.x - M) * kLog2e);
+        }
+        const float lse = M + __builtin_amdgcn_logf(S) * kLn2;
+        lse_s[b] = lse;
+        if (p.lse_out) p.lse_out[row] = lse;
+    }
+    const int n = *req_cnt(p, r);
+    const uint64_t* in = p.stage1 + (int64_t)r * p.list_cap;
+    const float* cum = p.cum + (int64_t)r * Win;
+    if (threadIdx.x == 0) {
+        s.cnt = 0;
+        s.thr = 0;
+    }
+    __syncthreads();
+    const int rounds = (n + kRound - 1) / kRound;
+    for (int rd = 0; rd < rounds; ++rd) {
+        const uint64_t thr = s.thr;
+        uint64_t keys[kPerThread];
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            const int i = rd * kRound + j * kTkThreads + threadIdx.x;
+            keys[j] = 0ull;
+            if (i < n) {
+                const uint64_t k = in[i];
+                const uint32_t f = 0xFFFFFFFFu - (uint32_t)k;
+                const int b = (int)(f / (uint32_t)V);
+                const float x = unorder_f32((uint32_t)(k >> 32));
+                keys[j] = make_key(cum[b] + (x - lse_s[b]), f);
+            }
+        }
+        insert(s, keys, thr);
+        __syncthreads();
+        if (s.cnt > kSoftCap) compact(s, W, p.err);
+    }
+    compact(s, W, p.err);
+    int S2 = 2;
+    while (S2 < W) S2 <<= 1;
+    sort_desc(s, min(s.cnt, W), S2);
+    for (int j = threadIdx.x; j < W; j += kTkThreads) {
+        const uint64_t key = s.buf[j];
+        const uint32_t f = 0xFFFFFFFFu - (uint32_t)key;
+        p.tokens[(int64_t)r * W + j] = (int32_t)(f % (uint32_t)V);
+        p.parent[(int64_t)r * W + j] = (int32_t)(f / (uint32_t)V);
+        p.cum_out[(int64_t)r * W + j] = unorder_f32((uint32_t)(key >> 32));
+    }
+    if (threadIdx.x < kSlot0 + kMaxSlots)       // leave the request's state line cleared
+        __hip_atomic_store(p.req_state + (int64_t)r * kTopkStateWords + threadIdx.x, 0ull, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace
+
+int64_t beam_topk_lists(int max_beams) {
+    // the merge on log-probs needs about max(max_beams, kTopkMaxChunks) slots;
+    // the merge on logits one more per beam row (every row boundary inside a
+    // range starts a piece of its own)
+    return std::max<int64_t>(max_beams, kTopkMaxChunks) + max_beams + 1;
+}
+
+int64_t beam_topk_parts_cap(int max_requests, int max_beams) {
+    // about one part per row plus two per stage-1 wave (16384 resident waves)
+    return (int64_t)max_requests * max_beams + 2 * 16384 + 64;
+}
 
 size_t beam_topk_workspace_bytes(int max_requests, int max_beams) {
     // per request: a 512-byte state line (threshold, append count, slots) and
-    // a list of up to max(max_beams, kTopkMaxChunks) * max_beams keys
-    const size_t per_req_lists = std::max<size_t>((size_t)max_beams, kTopkMaxChunks);
-    return (size_t)max_requests * (kTopkStateWords + per_req_lists * max_beams) * sizeof(uint64_t);
+    // a list of beam_topk_lists(max_beams) * max_beams keys; then the parts
+    // of the merge on logits
+    return (size_t)max_requests * (kTopkStateWords + (size_t)beam_topk_lists(max_beams) * max_beams) *
+               sizeof(uint64_t) +
+           (size_t)beam_topk_parts_cap(max_requests, max_beams) * sizeof(float2);
 }
 
 size_t beam_topk_stage1_lds(int width) {
@@ -770,6 +985,61 @@ hipError_t launch_beam_topk_merge(const TopkParams& p, hipStream_t stream) {
         (void)hipMemset(p.req_state, 0, sizeof(uint64_t) * kTopkStateWords * (size_t)p.num_requests);
     }
     return e;
+}
+
+int64_t beam_topk_logits_segment(int num_requests, int beams_in, int vocab, int64_t resident_waves, int64_t lists,
+                                 int64_t parts_cap, int& rpw) {
+    const int64_t total = (int64_t)num_requests * beams_in * vocab;
+    const int64_t req_len = (int64_t)beams_in * vocab;
+    int64_t seg = (total + resident_waves - 1) / std::max<int64_t>(1, resident_waves);
+    seg = std::max<int64_t>(seg, kTopkMinSegment);
+    // the pieces of one request: at most ceil(req_len / seg) + 1 ranges overlap
+    // it, and each of its beams_in - 1 inner row boundaries splits one more
+    const int64_t free_slots = std::max<int64_t>(1, lists - beams_in - 1);
+    seg = std::max<int64_t>(seg, (req_len + free_slots - 1) / free_slots);
+    seg = (seg + 3) & ~(int64_t)3;
+    for (;;) {
+        const int64_t waves = (total + seg - 1) / seg;
+        const int64_t per = (seg - 1) / vocab + 2;              // rows one range can touch
+        if (waves * per <= parts_cap || seg >= total) {
+            rpw = (int)per;
+            return seg;
+        }
+        seg = (2 * seg + 3) & ~(int64_t)3;
+    }
+}
+
+hipError_t launch_beam_topk_merge_logits(const TopkParams& p, hipStream_t stream) {
+    if (p.num_requests == 0) return hipSuccess;
+    const bool vec = (p.vocab % 4 == 0) && (((uintptr_t)p.logprobs & 15) == 0);
+    const int64_t total = (int64_t)p.num_requests * p.beams_in * p.vocab;
+    const int64_t waves = (total + p.seg - 1) / p.seg;
+    const int64_t blocks = (waves + kTkThreads / kWLanes - 1) / (kTkThreads / kWLanes);
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    const size_t lds = beam_topk_stage1_lds(p.width);
+    if (vec)
+        hipLaunchKernelGGL(topk_logits_stage1_kernel<true>, dim3((unsigned)blocks), dim3(kTkThreads), lds, stream, p);
+    else
+        hipLaunchKernelGGL(topk_logits_stage1_kernel<false>, dim3((unsigned)blocks), dim3(kTkThreads), lds, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_logits_stage2_kernel, dim3(p.num_requests), dim3(kTkThreads), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) {
+        (void)hipStreamSynchronize(stream);
+        (void)hipMemset(p.req_state, 0, sizeof(uint64_t) * kTopkStateWords * (size_t)p.num_requests);
+    }
+    return e;
+}
+
+int beam_topk_logits_blocks_per_cu(int width) {
+    int n = 0;
+    const size_t lds = beam_topk_stage1_lds(width);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)topk_logits_stage1_kernel<true>, kTkThreads,
+                                                     lds) != hipSuccess ||
+        n <= 0)
+        n = 1;
+    return n;
 }
 
 int beam_topk_blocks_per_cu(int width) {

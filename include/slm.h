@@ -178,6 +178,32 @@ slm_status slm_beam_topk_merge(slm_ctx *ctx, const float *logprobs, const float 
                                float *cum_out);
 
 /*
+ * Beam top-k merge on logits: the merge above with each beam row's
+ * log-softmax folded in, so the log-probabilities are never written (§1.1:
+ * the fixed beam-search node takes the model's output straight into the
+ * merge).
+ *   logits [R, Win, V] fp32, cum [R, Win] fp32 (device)
+ *   tokens, parent [R, W] int32; cum_out [R, W] fp32; lse_out [R, Win] fp32
+ *   or NULL (each row's log-sum-exp, for inspection)
+ * For row (r, b): lse = log sum_v exp(logits[r,b,v]), computed in fp32 from
+ * the row's maximum (approximate: exp and log by the hardware's fp32
+ * instructions, partial sums combined in a fixed order, so repeated calls
+ * agree bitwise).  Candidate (b, v) scores cum[r,b] + (logits[r,b,v] - lse),
+ * two fp32 operations; ranking, tie rule and outputs are those of
+ * slm_beam_topk_merge on these scores.  Candidates whose exact scores are
+ * closer than the lse's error may therefore rank in either order.
+ * Logits must be finite or -inf, above -1e30, with a finite one in every
+ * row.  Needs 1 <= W <= Win*V, W <= 512, Win <= 512, Win*V < 2^31, R <=
+ * caps.max_requests, Win, W <= caps.max_beams, V <= caps.max_vocab.
+ * Outputs must not overlap the inputs or each other.  The logits are read
+ * once (one HBM pass); the call allocates nothing.
+ */
+slm_status slm_beam_topk_merge_logits(slm_ctx *ctx, const float *logits, const float *cum,
+                                      int32_t num_requests, int32_t beams_in, int32_t vocab,
+                                      int32_t width, int32_t *tokens, int32_t *parent,
+                                      float *cum_out, float *lse_out);
+
+/*
  * Suffix K/V reorder after a merge (§1.1 parent index, §1.2 per-beam suffix):
  *   k_out[l,r,j,i] = k_in[l,r,parent[r,j],i] for rows i < rows, same for V;
  *   [NL, R, W, S_cap, Hkv, D] bf16 storage.  Rows >= rows are untouched.

@@ -84,6 +84,30 @@ def test_topk_validation(dry):
     assert _status(lambda: dry.beam_topk_merge(buf.view(2, 3, 50), cum, 4, tokens=tok)) == slm.SLM_ERR_ALIAS
 
 
+def test_topk_logits_validation(dry):
+    x = torch.zeros((2, 3, 50), dtype=torch.float32)
+    cum = torch.zeros((2, 3), dtype=torch.float32)
+    lse = torch.zeros((2, 3), dtype=torch.float32)
+    assert _status(lambda: dry.beam_topk_merge_logits(x, cum, 4)) == slm.SLM_OK
+    assert _status(lambda: dry.beam_topk_merge_logits(x, cum, 4, lse_out=lse)) == slm.SLM_OK
+    assert _status(lambda: dry.beam_topk_merge_logits(x, cum, 151)) == slm.SLM_ERR_INVALID_ARG   # W > Win*V
+    assert _status(lambda: dry.beam_topk_merge_logits(torch.zeros((2, 3, 500)), cum, 513)) \
+        == slm.SLM_ERR_UNSUPPORTED
+    wide = slm.Context(device=-1, max_beams=600)
+    assert _status(lambda: wide.beam_topk_merge_logits(torch.zeros((1, 513, 2)), torch.zeros((1, 513)), 4)) \
+        == slm.SLM_ERR_UNSUPPORTED                                  # Win above 512
+    small = slm.Context(device=-1, max_requests=1)
+    assert _status(lambda: small.beam_topk_merge_logits(x, cum, 4)) == slm.SLM_ERR_CAPACITY
+    buf = torch.zeros(2 * 3 * 50, dtype=torch.float32)
+    tok = buf[:8].view(torch.int32).view(2, 4)                  # overlaps the logits
+    assert _status(lambda: dry.beam_topk_merge_logits(buf.view(2, 3, 50), cum, 4, tokens=tok)) == slm.SLM_ERR_ALIAS
+    cl = torch.zeros(12, dtype=torch.float32)
+    assert _status(lambda: dry.beam_topk_merge_logits(x, cl[:6].view(2, 3), 4, lse_out=cl[3:9].view(2, 3))) \
+        == slm.SLM_ERR_ALIAS                                        # lse_out overlaps cum
+    with pytest.raises(ValueError):
+        dry.beam_topk_merge_logits(x, cum, 4, lse_out=torch.zeros((3, 2)))
+
+
 def _beam_args(NL=2, R=2, W=3, P=5, S=4, Hq=4, Hkv=2, D=64):
     return dict(q=_bf(NL, R, W, Hq, D), prefix_k=_bf(NL, R, P, Hkv, D), prefix_v=_bf(NL, R, P, Hkv, D),
                 suffix_k_in=_bf(NL, R, W, S, Hkv, D), suffix_v_in=_bf(NL, R, W, S, Hkv, D),

@@ -131,6 +131,11 @@ def normal_bf16(base: int, tid: int, shape: Sequence[int], layer: int = 0,
     return f32_to_bf16_bits(x)
 
 
+def logits(base: int, shape: Sequence[int], step: int = 0) -> np.ndarray:
+    """fp32 N(0,1) logits: the draw the log-probs below are made from."""
+    return _rng(base, TID_LOGITS, 0, step).standard_normal(tuple(shape), dtype=np.float32)
+
+
 def logprobs(base: int, shape: Sequence[int], step: int = 0) -> np.ndarray:
     """fp32 log-probs: N(0,1) fp32 logits, log-softmax over the last axis in
     fp64, one rounding to fp32."""
@@ -191,6 +196,14 @@ def torch_normal_bf16(shape, seed_tuple, device):
     g.manual_seed(_fold_seed(seed_tuple))
     x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
     return x.to(torch.bfloat16)   # round to nearest even
+
+
+def torch_logits(shape, seed_tuple, device):
+    """fp32 N(0,1) logits drawn on ``device`` (the draw torch_logprobs normalises)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(_fold_seed(seed_tuple))
+    return torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
 
 
 def torch_logprobs(shape, seed_tuple, device):
