@@ -100,11 +100,21 @@ struct TopkParams {
     int64_t seg;                        // candidates per stage-1 wave (a multiple of 4)
     int num_requests, beams_in, vocab, width;
     // merge on logits only (logprobs then holds the logits):
-    float2* parts;                      // workspace: per (stage-1 wave, row it touches) (max, sum of exp)
+    struct Piece {                      // one row's part of one stage-1 range
+        float m, s;                     // max logit, sum of exp(x - m)
+        int base, count;                // its kept keys in the request's list
+    };
+    Piece* parts;                       // workspace: per (stage-1 wave, row it touches)
+    uint64_t* level2;                   // workspace: [R, kTopkLogitChunks, list W] first-level top W per chunk
+    int* level2_cnt;                    // workspace: [R, kTopkLogitChunks] keys in each
     float* lse_out;                     // [R, Win] each row's log-sum-exp, or null
     int rpw;                            // part slots per stage-1 wave: rows one wave can touch
+    int rows_per_chunk, chunks;         // first-level chunks of beam rows per request
+    int level2_w;                       // key slots per chunk in level2 (max_beams)
     int* err;                           // device error flag
 };
+constexpr int kTopkLogitChunks = 64;    // first-level chunks per request at most
+constexpr int kTopkChunkPieces = 512;   // pieces per first-level chunk at most
 hipError_t launch_beam_topk_merge(const TopkParams& p, hipStream_t stream);
 hipError_t launch_beam_topk_merge_logits(const TopkParams& p, hipStream_t stream);
 size_t beam_topk_workspace_bytes(int max_requests, int max_beams);
@@ -114,7 +124,7 @@ int64_t beam_topk_parts_cap(int max_requests, int max_beams);
 // every piece (one row's part of one range) taking a list slot, and the waves'
 // part slots within parts_cap; sets rpw
 int64_t beam_topk_logits_segment(int num_requests, int beams_in, int vocab, int64_t resident_waves, int64_t lists,
-                                 int64_t parts_cap, int& rpw);
+                                 int64_t parts_cap, int& rpw, int& rows_per_chunk, int& chunks);
 int beam_topk_logits_blocks_per_cu(int width);
 // candidates per stage-1 wave: the call split evenly over the resident waves,
 // at least kTopkMinSegment, and few enough ranges per request for its list

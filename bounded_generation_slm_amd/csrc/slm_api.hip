@@ -437,13 +437,20 @@ slm_status slm_beam_topk_merge_logits(slm_ctx* ctx, const float* logits, const f
     p.req_state = ctx->topk_ws;
     p.stage1 = ctx->topk_ws + slm::kTopkStateWords * R_cap;
     p.list_cap = ctx->topk_lists * ctx->caps.max_beams;
-    p.parts = (float2*)(p.stage1 + R_cap * p.list_cap);
+    p.parts = (slm::TopkParams::Piece*)(p.stage1 + R_cap * p.list_cap);
+    const int64_t parts_cap = slm::beam_topk_parts_cap(ctx->caps.max_requests, ctx->caps.max_beams);
+    p.level2 = (uint64_t*)(p.parts + parts_cap);
+    p.level2_w = ctx->caps.max_beams;
+    p.level2_cnt = (int*)(p.level2 + R_cap * slm::kTopkLogitChunks * p.level2_w);
     p.num_requests = num_requests; p.beams_in = beams_in; p.vocab = vocab; p.width = width;
     int& bpc = ctx->topk_logits_blocks_per_cu[width];
     if (bpc == 0) bpc = ctx->dry_run ? 1 : slm::beam_topk_logits_blocks_per_cu(width);
     const int64_t resident = (int64_t)ctx->num_cus * bpc * 4;
-    p.seg = slm::beam_topk_logits_segment(num_requests, beams_in, vocab, resident, ctx->topk_lists,
-                                          slm::beam_topk_parts_cap(ctx->caps.max_requests, ctx->caps.max_beams), p.rpw);
+    p.seg = slm::beam_topk_logits_segment(num_requests, beams_in, vocab, resident, ctx->topk_lists, parts_cap, p.rpw,
+                                          p.rows_per_chunk, p.chunks);
+    if (p.chunks > slm::kTopkLogitChunks || p.rows_per_chunk > 256 ||
+        (int64_t)p.rows_per_chunk * ((vocab - 1) / p.seg + 2) > slm::kTopkChunkPieces)
+        return fail(ctx, SLM_ERR_UNSUPPORTED, "topk_logits: no first-level chunking fits this shape");
     return SLM_LAUNCH(ctx, slm::launch_beam_topk_merge_logits(p, ctx->stream), "topk_logits");
 }
 

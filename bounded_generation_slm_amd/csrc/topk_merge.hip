@@ -845,7 +845,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_logits_stage1_kernel(const To
         float S = ls * fast_exp2((lm - M) * kLog2e);
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off);
-        if (lane == 0) p.parts[part_slot(wid, row, p.seg, V, p.rpw)] = float2{M, S};
         // the piece's W largest keys go to request r's list
         wave_fence();
         if (cnt > W) shrink();
@@ -854,35 +853,115 @@ __global__ __launch_bounds__(kTkThreads) void topk_logits_stage1_kernel(const To
         base = __shfl(base, 0);
         uint64_t* list = p.stage1 + (int64_t)r * p.list_cap;
         for (int i = lane; i < cnt; i += kWLanes) list[base + i] = buf[i];
+        if (lane == 0) p.parts[part_slot(wid, row, p.seg, V, p.rpw)] = TopkParams::Piece{M, S, base, cnt};
         wave_fence();
         a = pe;
     }
 }
 
-// Stage 2 of the merge on logits: per request, the rows' lse from their
-// pieces (in piece order), then the kept candidates re-keyed by score.
-__global__ __launch_bounds__(kTkThreads) void topk_logits_stage2_kernel(const TopkParams p) {
+// Stage 2 of the merge on logits, first level: one workgroup per (chunk of
+// beam rows, request).  Each row's lse from its pieces (in piece order), then
+// the rows' kept candidates re-keyed by score and reduced to the chunk's top
+// W, written unsorted to the chunk's level-2 slot.
+__global__ __launch_bounds__(kTkThreads) void topk_logits_chunk_kernel(const TopkParams p) {
     __shared__ SelectorLds s;
-    __shared__ float lse_s[kTopkMaxWidth];
-    const int r = blockIdx.x;
+    __shared__ float lse_s[kTkThreads];
+    __shared__ int first_s[kTkThreads + 1];                 // first piece of each row (prefix over rows)
+    __shared__ int pbase[kTopkChunkPieces];
+    __shared__ int pfx[kTopkChunkPieces + 1];               // prefix of the pieces' key counts
+    const int c = blockIdx.x, r = blockIdx.y;
     const int W = p.width, V = p.vocab, Win = p.beams_in;
-    for (int b = threadIdx.x; b < Win; b += kTkThreads) {
+    const int b0 = c * p.rows_per_chunk, b1 = min(Win, b0 + p.rows_per_chunk);
+    const int tid = threadIdx.x;
+    // rows: lse and piece counts (rows_per_chunk <= kTkThreads: one row per thread)
+    int npieces = 0;
+    int64_t w0 = 0;
+    const int b = b0 + tid;
+    if (b < b1) {
         const int64_t row = (int64_t)r * Win + b;
-        const int64_t w0 = row * V / p.seg, w1 = (row * V + V - 1) / p.seg;
+        w0 = row * V / p.seg;
+        const int64_t w1 = (row * V + V - 1) / p.seg;
+        npieces = (int)(w1 - w0 + 1);
         float M = kLogitFloor;
-        for (int64_t w = w0; w <= w1; ++w) M = fmaxf(M, p.parts[part_slot(w, row, p.seg, V, p.rpw)].x);
+        for (int64_t w = w0; w <= w1; ++w) M = fmaxf(M, p.parts[part_slot(w, row, p.seg, V, p.rpw)].m);
         float S = 0.f;
         for (int64_t w = w0; w <= w1; ++w) {
-            const float2 q = p.parts[part_slot(w, row, p.seg, V, p.rpw)];
-            S += q.y * fast_exp2((q.x - M) * kLog2e);
+            const TopkParams::Piece q = p.parts[part_slot(w, row, p.seg, V, p.rpw)];
+            S += q.s * fast_exp2((q.m - M) * kLog2e);
         }
         const float lse = M + __builtin_amdgcn_logf(S) * kLn2;
-        lse_s[b] = lse;
+        lse_s[tid] = lse;
         if (p.lse_out) p.lse_out[row] = lse;
     }
-    const int n = *req_cnt(p, r);
+    const int incl = block_inclusive_scan(npieces, s);
+    first_s[tid + 1] = incl;
+    if (tid == 0) first_s[0] = 0;
+    __syncthreads();
+    const int total_pieces = first_s[kTkThreads];           // <= kTopkChunkPieces (host sizing)
+    if (b < b1) {
+        const int64_t row = (int64_t)r * Win + b;
+        for (int j = 0; j < npieces; ++j) {
+            const TopkParams::Piece q = p.parts[part_slot(w0 + j, row, p.seg, V, p.rpw)];
+            pbase[first_s[tid] + j] = q.base;
+            pfx[first_s[tid] + j + 1] = q.count;
+        }
+    }
+    if (tid == 0) {
+        pfx[0] = 0;
+        s.cnt = 0;
+        s.thr = 0;
+    }
+    __syncthreads();
+    // prefix of the counts (two entries per thread)
+    {
+        const int i0 = 1 + 2 * tid, i1 = i0 + 1;
+        const int v0 = i0 <= total_pieces ? pfx[i0] : 0, v1 = i1 <= total_pieces ? pfx[i1] : 0;
+        const int inc = block_inclusive_scan(v0 + v1, s);
+        if (i0 <= total_pieces) pfx[i0] = inc - v1;
+        if (i1 <= total_pieces) pfx[i1] = inc;
+    }
+    __syncthreads();
+    const int n = pfx[total_pieces];
     const uint64_t* in = p.stage1 + (int64_t)r * p.list_cap;
     const float* cum = p.cum + (int64_t)r * Win;
+    const int rounds = (n + kRound - 1) / kRound;
+    for (int rd = 0; rd < rounds; ++rd) {
+        const uint64_t thr = s.thr;
+        uint64_t keys[kPerThread];
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            const int i = rd * kRound + j * kTkThreads + tid;
+            keys[j] = 0ull;
+            if (i < n) {
+                int lo = 0, hi = total_pieces - 1;              // the piece holding key i: pfx[k] <= i < pfx[k+1]
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (pfx[mid] <= i) lo = mid; else hi = mid - 1;
+                }
+                const uint64_t k = in[pbase[lo] + (i - pfx[lo])];
+                const uint32_t f = 0xFFFFFFFFu - (uint32_t)k;
+                const int bb = (int)(f / (uint32_t)V);
+                const float x = unorder_f32((uint32_t)(k >> 32));
+                keys[j] = make_key(cum[bb] + (x - lse_s[bb - b0]), f);
+            }
+        }
+        insert(s, keys, thr);
+        __syncthreads();
+        if (s.cnt > kSoftCap) compact(s, W, p.err);
+    }
+    compact(s, W, p.err);
+    const int kept = min(s.cnt, W);
+    uint64_t* out = p.level2 + ((int64_t)r * kTopkLogitChunks + c) * p.level2_w;
+    for (int j = tid; j < kept; j += kTkThreads) out[j] = s.buf[j];
+    if (tid == 0) p.level2_cnt[r * kTopkLogitChunks + c] = kept;
+}
+
+// Second level: per request, the chunks' keys -> the final W, sorted.
+__global__ __launch_bounds__(kTkThreads) void topk_logits_final_kernel(const TopkParams p) {
+    __shared__ SelectorLds s;
+    const int r = blockIdx.x;
+    const int W = p.width, V = p.vocab;
+    const int n = p.chunks * W;                             // chunk c's keys at [c*W, c*W + cnt_c)
     if (threadIdx.x == 0) {
         s.cnt = 0;
         s.thr = 0;
@@ -897,11 +976,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_logits_stage2_kernel(const To
             const int i = rd * kRound + j * kTkThreads + threadIdx.x;
             keys[j] = 0ull;
             if (i < n) {
-                const uint64_t k = in[i];
-                const uint32_t f = 0xFFFFFFFFu - (uint32_t)k;
-                const int b = (int)(f / (uint32_t)V);
-                const float x = unorder_f32((uint32_t)(k >> 32));
-                keys[j] = make_key(cum[b] + (x - lse_s[b]), f);
+                const int c = i / W, e = i - c * W;
+                if (e < p.level2_cnt[r * kTopkLogitChunks + c])
+                    keys[j] = p.level2[((int64_t)r * kTopkLogitChunks + c) * p.level2_w + e];
             }
         }
         insert(s, keys, thr);
@@ -940,11 +1017,13 @@ int64_t beam_topk_parts_cap(int max_requests, int max_beams) {
 
 size_t beam_topk_workspace_bytes(int max_requests, int max_beams) {
     // per request: a 512-byte state line (threshold, append count, slots) and
-    // a list of beam_topk_lists(max_beams) * max_beams keys; then the parts
-    // of the merge on logits
+    // a list of beam_topk_lists(max_beams) * max_beams keys; then, for the
+    // merge on logits, the pieces, the level-2 keys and their counts
     return (size_t)max_requests * (kTopkStateWords + (size_t)beam_topk_lists(max_beams) * max_beams) *
                sizeof(uint64_t) +
-           (size_t)beam_topk_parts_cap(max_requests, max_beams) * sizeof(float2);
+           (size_t)beam_topk_parts_cap(max_requests, max_beams) * sizeof(TopkParams::Piece) +
+           (size_t)max_requests * kTopkLogitChunks * max_beams * sizeof(uint64_t) +
+           (size_t)max_requests * kTopkLogitChunks * sizeof(int);
 }
 
 size_t beam_topk_stage1_lds(int width) {
@@ -988,7 +1067,7 @@ hipError_t launch_beam_topk_merge(const TopkParams& p, hipStream_t stream) {
 }
 
 int64_t beam_topk_logits_segment(int num_requests, int beams_in, int vocab, int64_t resident_waves, int64_t lists,
-                                 int64_t parts_cap, int& rpw) {
+                                 int64_t parts_cap, int& rpw, int& rows_per_chunk, int& chunks) {
     const int64_t total = (int64_t)num_requests * beams_in * vocab;
     const int64_t req_len = (int64_t)beams_in * vocab;
     int64_t seg = (total + resident_waves - 1) / std::max<int64_t>(1, resident_waves);
@@ -1001,8 +1080,19 @@ int64_t beam_topk_logits_segment(int num_requests, int beams_in, int vocab, int6
     for (;;) {
         const int64_t waves = (total + seg - 1) / seg;
         const int64_t per = (seg - 1) / vocab + 2;              // rows one range can touch
-        if (waves * per <= parts_cap || seg >= total) {
+        // first-level chunks: about 256 workgroups over the call, at most
+        // kTkThreads rows and kTopkChunkPieces pieces each, kTopkLogitChunks
+        // per request
+        const int64_t ppr = (vocab - 1) / seg + 2;              // pieces one row can have
+        int64_t rpc = ((int64_t)num_requests * beams_in + 255) / 256;
+        rpc = std::min<int64_t>(std::max<int64_t>(rpc, 1), 256);
+        rpc = std::min<int64_t>(rpc, std::max<int64_t>(1, kTopkChunkPieces / ppr));
+        rpc = std::max<int64_t>(rpc, (beams_in + kTopkLogitChunks - 1) / kTopkLogitChunks);
+        const bool chunks_fit = rpc <= 256 && rpc * ppr <= kTopkChunkPieces;
+        if ((waves * per <= parts_cap && chunks_fit) || seg >= total) {
             rpw = (int)per;
+            rows_per_chunk = (int)rpc;
+            chunks = (int)((beams_in + rpc - 1) / rpc);
             return seg;
         }
         seg = (2 * seg + 3) & ~(int64_t)3;
@@ -1023,8 +1113,12 @@ hipError_t launch_beam_topk_merge_logits(const TopkParams& p, hipStream_t stream
         hipLaunchKernelGGL(topk_logits_stage1_kernel<false>, dim3((unsigned)blocks), dim3(kTkThreads), lds, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_logits_stage2_kernel, dim3(p.num_requests), dim3(kTkThreads), 0, stream, p);
+    hipLaunchKernelGGL(topk_logits_chunk_kernel, dim3(p.chunks, p.num_requests), dim3(kTkThreads), 0, stream, p);
     e = hipGetLastError();
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(topk_logits_final_kernel, dim3(p.num_requests), dim3(kTkThreads), 0, stream, p);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) {
         (void)hipStreamSynchronize(stream);
         (void)hipMemset(p.req_state, 0, sizeof(uint64_t) * kTopkStateWords * (size_t)p.num_requests);
