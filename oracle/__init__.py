@@ -53,9 +53,10 @@ def _load():
         lib.orc_beam_decode_attn.argtypes = [i32] * 9 + [f64] + [P] * 11
         lib.orc_topk_merge.argtypes = [P, P, i32, i32, i32, i32, P, P, P]
         lib.orc_topk_merge_logits.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P]
+        lib.orc_label_head.argtypes = [P, P, i32, i32, P, i32, P, i32, i32, P, P, P, P, P, P]
         lib.orc_reorder_suffix.argtypes = [i32] * 7 + [P] * 5
         for f in ("orc_prefill_attn", "orc_prefill_attn_rows", "orc_gather_last",
-                  "orc_beam_decode_attn", "orc_topk_merge", "orc_topk_merge_logits",
+                  "orc_beam_decode_attn", "orc_topk_merge", "orc_topk_merge_logits", "orc_label_head",
                   "orc_reorder_suffix"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
@@ -111,6 +112,27 @@ def gather_last(hidden, cu_seqlens) -> np.ndarray:
     out = np.empty((B, H), np.uint16)
     _check(_load().orc_gather_last(_p(hidden), _p(cu), B, H, _p(out)), "gather_last")
     return out
+
+
+def label_head(hidden, cu_seqlens, lm_head, labels, k, label_map=None):
+    """Prefill-only label head.  hidden [T,H], lm_head [V,H] 16-bit storage;
+    labels [L] token ids; optional label_map [L] int32.  Returns (logits [B,L]
+    fp64, probs [B,L] fp64, top_idx [B,K] int32, top_prob [B,K] fp64,
+    top_class [B,K] int32 (map[top_idx], or top_idx without a map))."""
+    hidden = _c(hidden, np.uint16)
+    lm = _c(lm_head, np.uint16)
+    cu = _c(cu_seqlens, np.int32)
+    lab = _c(labels, np.int32)
+    mp = None if label_map is None else _c(label_map, np.int32)
+    B, H, V, L, K = len(cu) - 1, hidden.shape[1], lm.shape[0], len(lab), int(k)
+    logits = np.empty((B, L), np.float64)
+    probs = np.empty((B, L), np.float64)
+    ti = np.empty((B, K), np.int32)
+    tp = np.empty((B, K), np.float64)
+    tc = np.empty((B, K), np.int32)
+    _check(_load().orc_label_head(_p(hidden), _p(cu), B, H, _p(lm), V, _p(lab), L, K, _p(mp), _p(logits),
+                                  _p(probs), _p(ti), _p(tp), _p(tc)), "label_head")
+    return logits, probs, ti, tp, tc
 
 
 def beam_decode_attn(q, prefix_k, prefix_v, suffix_k_in, suffix_v_in, k_new, v_new,

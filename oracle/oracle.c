@@ -16,7 +16,10 @@
  *     (§1.1);
  *   - the same merge taking each beam row's logits, with the row's
  *     log-softmax folded in (the next step the page's fixed beam-search
- *     node runs on the model's output, §1.1).
+ *     node runs on the model's output, §1.1);
+ *   - the prefill-only label head: the next-token logits of the target
+ *     label tokens at each sequence's last valid token, then softmax, top-K
+ *     and a fixed mapping (§1.1, prefill-only models).
  * Where the page is silent the readings are: GQA query head h reads KV head
  * floor(h*Hkv/Hq); softmax scale is a parameter (1/sqrt(D) in every workload);
  * the causal boundary includes the diagonal; candidate score is one IEEE fp32
@@ -141,6 +144,63 @@ int orc_gather_last(const uint16_t *hidden, const int32_t *cu, int B, int H,
                    sizeof(uint16_t) * (size_t)H);
         else
             memset(out + (int64_t)b * H, 0, sizeof(uint16_t) * (size_t)H);
+    }
+    return 0;
+}
+
+/* Prefill-only label head.  For sequence b, h = its last valid hidden row
+ * (zero for an empty sequence); for label j, z[b,j] = h . lm[label[j]] (fp64
+ * over the 16-bit-storage values); p[b,:] = softmax over the L label logits
+ * (fp64, shifted by the row maximum); the K labels with the largest logits,
+ * ties to the lower label index, in that order: their index j and
+ * probability; with a map, class[b,k] = map[j].  hidden [T,H], lm [V,H]
+ * bf16 storage; label [L] token ids. */
+int orc_label_head(const uint16_t *hidden, const int32_t *cu, int B, int H,
+                   const uint16_t *lm, int V, const int32_t *label, int L, int K,
+                   const int32_t *map, double *logits, double *probs,
+                   int32_t *top_idx, double *top_prob, int32_t *top_class)
+{
+    if (B < 0 || H <= 0 || V <= 0 || L <= 0 || K <= 0 || K > L)
+        return 1;
+    for (int j = 0; j < L; ++j)
+        if (label[j] < 0 || label[j] >= V)
+            return 1;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int b = 0; b < B; ++b) {
+        const int64_t last = cu[b + 1] > cu[b] ? (int64_t)cu[b + 1] - 1 : -1;
+        double *z = logits + (int64_t)b * L;
+        double m = -INFINITY;
+        for (int j = 0; j < L; ++j) {
+            double acc = 0.0;
+            if (last >= 0) {
+                const uint16_t *hr = hidden + last * H, *wr = lm + (int64_t)label[j] * H;
+                for (int d = 0; d < H; ++d)
+                    acc += bf16_to_f64(hr[d]) * bf16_to_f64(wr[d]);
+            }
+            z[j] = acc;
+            if (acc > m)
+                m = acc;
+        }
+        double s = 0.0;
+        for (int j = 0; j < L; ++j)
+            s += exp(z[j] - m);
+        for (int j = 0; j < L; ++j)
+            probs[(int64_t)b * L + j] = exp(z[j] - m) / s;
+        /* top K by selection: each pick is the largest logit not yet taken,
+         * the lower index first among equals */
+        unsigned char *taken = calloc((size_t)L, 1);
+        for (int k = 0; k < K; ++k) {
+            int best = -1;
+            for (int j = 0; j < L; ++j)
+                if (!taken[j] && (best < 0 || z[j] > z[best]))
+                    best = j;
+            taken[best] = 1;
+            top_idx[(int64_t)b * K + k] = best;
+            top_prob[(int64_t)b * K + k] = probs[(int64_t)b * L + best];
+            if (top_class)
+                top_class[(int64_t)b * K + k] = map ? map[best] : best;
+        }
+        free(taken);
     }
     return 0;
 }
