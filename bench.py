@@ -182,6 +182,32 @@ def extra_workloads(ctx, dev, ev, reps=5):
         "us_per_request_median": round(us, 1), "tokens_per_s": round(T / (us * 1e-6), 1),
         "hbm_frac": round(pbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "mfma_frac": round(pflops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    # the prefill-only label head after the gather: 64 label rows of a synthetic
+    # 151,936-row LM head, top 5, on this request and on the 960-sequence pack
+    V = 151936
+    g_lm = torch.Generator(device=dev)
+    g_lm.manual_seed(29)
+    lm = (torch.randn((V, pr.hidden_dim), generator=g_lm, device=dev) * pr.hidden_dim ** -0.5).to(torch.bfloat16)
+    labels = torch.from_numpy(wl.label_ids(pr.base_seed, V)).to(dev)
+    pf = wl.PREFILL_THROUGHPUT
+    hid_pf = wl.torch_normal_bf16((pf.total_tokens, pf.hidden_dim), (pf.base_seed, wl.TID_HIDDEN, 0, 0), dev)
+    cu_pf = torch.from_numpy(pf.cu_seqlens()).to(dev)
+    for name, hh, cc, nseq in (("label_head_prefill_request", hidden, cu, len(pr.lengths)),
+                               ("label_head_prefill_throughput", hid_pf, cu_pf, len(pf.lengths))):
+        for _ in range(3):
+            ctx.label_head(hh, cc, lm, labels, wl.LABEL_TOP_K)
+        times = []
+        for _ in range(reps * 4):
+            e0 = ev()
+            ctx.label_head(hh, cc, lm, labels, wl.LABEL_TOP_K)
+            times.append((e0, ev()))
+        torch.cuda.synchronize()
+        ctx.check()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in times)[len(times) // 2]
+        res[name] = {"workload": "%d sequences, hidden %d, %d labels of a %d-row LM head, top %d" % (
+            nseq, pr.hidden_dim, wl.LABEL_COUNT, V, wl.LABEL_TOP_K), "us_median": round(us, 1),
+            "sequences_per_s": round(nseq / (us * 1e-6), 1)}
+    del lm, hid_pf
     del q, k, v, hidden, out
     # the long-prompt wide beam search
     bl = BeamRun(wl.BEAM_LONG, dev)

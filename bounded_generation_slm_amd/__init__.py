@@ -38,7 +38,7 @@ EXPORTED = (
     "slm_abi_version", "slm_status_string", "slm_ctx_create", "slm_ctx_destroy",
     "slm_ctx_set_stream", "slm_ctx_check", "slm_ctx_last_error", "slm_packed_prefill_attn",
     "slm_gather_last", "slm_beam_decode_attn", "slm_beam_topk_merge", "slm_beam_topk_merge_logits",
-    "slm_beam_reorder_suffix",
+    "slm_beam_reorder_suffix", "slm_label_head",
 )
 
 
@@ -73,10 +73,11 @@ _lib.slm_gather_last.argtypes = [_P, _P, _P, _I, _I, _I, ctypes.c_int, _P]
 _lib.slm_beam_decode_attn.argtypes = [_P, ctypes.POINTER(_BeamAttnArgs)]
 _lib.slm_beam_topk_merge.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]
 _lib.slm_beam_topk_merge_logits.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P]
+_lib.slm_label_head.argtypes = [_P, _P, _P, _I, _I, _I, _P, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P]
 _lib.slm_beam_reorder_suffix.argtypes = [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
 for _name in ("slm_ctx_create", "slm_ctx_set_stream", "slm_ctx_check", "slm_packed_prefill_attn",
               "slm_gather_last", "slm_beam_decode_attn", "slm_beam_topk_merge", "slm_beam_topk_merge_logits",
-              "slm_beam_reorder_suffix"):
+              "slm_beam_reorder_suffix", "slm_label_head"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -180,6 +181,10 @@ class Context:
 
     def beam_reorder_suffix(self, parent, k_in, v_in, rows: int, k_out, v_out):
         return slm_beam_reorder_suffix(self, parent, k_in, v_in, rows, k_out, v_out)
+
+    def label_head(self, hidden, cu_seqlens, lm_head, labels, k: int, label_map=None, probs: bool = True,
+                   out=None):
+        return slm_label_head(self, hidden, cu_seqlens, lm_head, labels, k, label_map, probs, out)
 
 
 def slm_packed_prefill_attn(ctx: Context, q, k, v, cu_seqlens, max_seqlen: int,
@@ -332,3 +337,32 @@ def slm_beam_reorder_suffix(ctx: Context, parent, k_in, v_in, rows: int, k_out, 
         _ptr(v_out, "v_out", _BF16, dev))
     ctx._raise(rc, "slm_beam_reorder_suffix")
     return k_out, v_out
+
+
+def slm_label_head(ctx: Context, hidden, cu_seqlens, lm_head, labels, k: int, label_map=None, probs: bool = True,
+                   out=None):
+    """hidden [T,H] bf16, cu_seqlens [B+1] int32, lm_head [V,H] bf16, labels [L] int32, optional
+    label_map [L] int32 -> (logits [B,L] f32, probs [B,L] f32 or None, top_idx [B,K] int32,
+    top_prob [B,K] f32, top_class [B,K] int32).  ``out`` may hold those five tensors."""
+    dev = ctx.device
+    T, H = hidden.shape
+    V = lm_head.shape[0]
+    if lm_head.shape[1] != H:
+        raise ValueError("lm_head must be [V, H] with the hidden size of hidden")
+    B, L, K = cu_seqlens.numel() - 1, labels.numel(), int(k)
+    if out is None:
+        out = (torch.empty((B, L), dtype=torch.float32, device=dev),
+               torch.empty((B, L), dtype=torch.float32, device=dev) if probs else None,
+               torch.empty((B, K), dtype=torch.int32, device=dev),
+               torch.empty((B, K), dtype=torch.float32, device=dev),
+               torch.empty((B, K), dtype=torch.int32, device=dev))
+    lg, pr, ti, tp, tc = out
+    ctx._stream()
+    rc = _lib.slm_label_head(
+        ctx._h, _ptr(hidden, "hidden", _BF16, dev), _ptr(cu_seqlens, "cu_seqlens", (torch.int32,), dev), B, T, H,
+        _ptr(lm_head, "lm_head", _BF16, dev), V, _ptr(labels, "labels", (torch.int32,), dev), L, K,
+        _ptr(label_map, "label_map", (torch.int32,), dev), _ptr(lg, "logits", (torch.float32,), dev),
+        _ptr(pr, "probs", (torch.float32,), dev), _ptr(ti, "top_idx", (torch.int32,), dev),
+        _ptr(tp, "top_prob", (torch.float32,), dev), _ptr(tc, "top_class", (torch.int32,), dev))
+    ctx._raise(rc, "slm_label_head")
+    return lg, pr, ti, tp, tc

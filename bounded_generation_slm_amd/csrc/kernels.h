@@ -12,6 +12,7 @@ enum DeviceError : int {
     kErrCuSeqlens = 1,     // cu_seqlens not monotone / out of [0,T] / length > max_seqlen
     kErrParent = 2,        // parent index outside [0, W)
     kErrSelect = 3,        // a top-k selection did not converge (equal keys: never for valid inputs)
+    kErrLabel = 4,         // a label token id outside [0, vocab)
 };
 
 
@@ -55,6 +56,25 @@ struct GatherParams {
     bool vec16;                         // 16-byte copies (row and pointers aligned)
 };
 hipError_t launch_gather_last(const GatherParams& p, hipStream_t stream);
+
+// Prefill-only label head: last-token hidden rows x label LM-head rows.
+struct LabelHeadParams {
+    const uint16_t* hidden;             // [T, H] bf16
+    const int32_t* cu;                  // [B + 1]
+    const uint16_t* lm;                 // [V, H] bf16 (only label rows read)
+    const int32_t* labels;              // [L] token ids
+    const int32_t* map;                 // [L] or null
+    float* logits;                      // [B, L]
+    float* probs;                       // [B, L] or null
+    int32_t* top_idx;                   // [B, K]
+    float* top_prob;                    // [B, K]
+    int32_t* top_class;                 // [B, K] or null
+    int* err;
+    int num_seqs, total_tokens, hidden_dim, vocab, num_labels, k;
+};
+hipError_t launch_label_head(const LabelHeadParams& p, hipStream_t stream);
+constexpr int kLabelMax = 4096;         // labels per call at most
+constexpr int kLabelTopMax = 64;        // K at most
 
 struct ReorderParams {
     const int32_t* parent;

@@ -199,6 +199,8 @@ slm_status slm_ctx_check(slm_ctx* ctx) {
         (void)hipMemset(ctx->err_flag, 0, sizeof(int));
         if (flag == slm::kErrCuSeqlens)
             return fail(ctx, SLM_ERR_INVALID_ARG, "cu_seqlens: not non-decreasing in [0,T] or a length above max_seqlen");
+        if (flag == slm::kErrLabel)
+            return fail(ctx, SLM_ERR_INVALID_ARG, "label_head: a label token id outside [0, vocab)");
         if (flag == slm::kErrSelect)
             return fail(ctx, SLM_ERR_DEVICE, "top-k: a selection pass limit was reached (equal keys)");
         return fail(ctx, SLM_ERR_INVALID_ARG, "parent index outside [0, width)");
@@ -285,6 +287,50 @@ slm_status slm_gather_last(slm_ctx* ctx, const void* hidden, const int32_t* cu_s
     if (((uintptr_t)hidden & 1) || ((uintptr_t)out & 1))
         return fail(ctx, SLM_ERR_INVALID_ARG, "gather: tensors must be 2-byte aligned");
     return SLM_LAUNCH(ctx, slm::launch_gather_last(p, ctx->stream), "gather");
+}
+
+slm_status slm_label_head(slm_ctx* ctx, const uint16_t* hidden, const int32_t* cu_seqlens, int32_t num_seqs,
+                          int32_t total_tokens, int32_t hidden_dim, const uint16_t* lm_head, int32_t vocab,
+                          const int32_t* labels, int32_t num_labels, int32_t k, const int32_t* label_map,
+                          float* logits, float* probs, int32_t* top_idx, float* top_prob, int32_t* top_class) {
+    slm_status s = enter(ctx);
+    if (s != SLM_OK) return s;
+    if (num_seqs < 0 || total_tokens < 0 || hidden_dim <= 0 || vocab <= 0 || num_labels <= 0 || k <= 0)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "label_head: a size is out of range");
+    if (k > num_labels) return fail(ctx, SLM_ERR_INVALID_ARG, "label_head: k %d > num_labels %d", k, num_labels);
+    if (hidden_dim % 16 != 0) return fail(ctx, SLM_ERR_UNSUPPORTED, "label_head: hidden_dim must be a multiple of 16");
+    if (num_labels > slm::kLabelMax || k > slm::kLabelTopMax)
+        return fail(ctx, SLM_ERR_UNSUPPORTED, "label_head: at most %d labels and k <= %d", slm::kLabelMax,
+                    slm::kLabelTopMax);
+    if (num_seqs == 0) return ok(ctx);
+    if (!cu_seqlens || !lm_head || !labels || !logits || !top_idx || !top_prob || (!hidden && total_tokens > 0))
+        return fail(ctx, SLM_ERR_INVALID_ARG, "label_head: NULL pointer");
+    if (!aligned16(hidden) || !aligned16(lm_head))
+        return fail(ctx, SLM_ERR_INVALID_ARG, "label_head: hidden and lm_head must be 16-byte aligned");
+    const void* four[] = {cu_seqlens, labels, label_map, logits, probs, top_idx, top_prob, top_class};
+    for (const void* q : four)
+        if ((uintptr_t)q & 3) return fail(ctx, SLM_ERR_INVALID_ARG, "label_head: tensors must be 4-byte aligned");
+    const size_t B = num_seqs, L = num_labels, K = k;
+    const size_t hb = (size_t)total_tokens * hidden_dim * 2, wb = (size_t)vocab * hidden_dim * 2;
+    struct Span { const void* p; size_t n; };
+    const Span ins[] = {{hidden, hb}, {lm_head, wb}, {cu_seqlens, (B + 1) * 4}, {labels, L * 4}, {label_map, L * 4}};
+    const Span outs[] = {{logits, B * L * 4}, {probs, B * L * 4}, {top_idx, B * K * 4}, {top_prob, B * K * 4},
+                         {top_class, B * K * 4}};
+    for (const Span& o : outs) {
+        if (!o.p) continue;
+        for (const Span& i : ins)
+            if (i.p && overlaps(o.p, o.n, i.p, i.n)) return fail(ctx, SLM_ERR_ALIAS, "label_head: an output overlaps an input");
+        for (const Span& o2 : outs)
+            if (&o2 != &o && o2.p && overlaps(o.p, o.n, o2.p, o2.n))
+                return fail(ctx, SLM_ERR_ALIAS, "label_head: outputs overlap each other");
+    }
+    slm::LabelHeadParams p{};
+    p.hidden = hidden; p.cu = cu_seqlens; p.lm = lm_head; p.labels = labels; p.map = label_map;
+    p.logits = logits; p.probs = probs; p.top_idx = top_idx; p.top_prob = top_prob; p.top_class = top_class;
+    p.err = ctx->err_flag;
+    p.num_seqs = num_seqs; p.total_tokens = total_tokens; p.hidden_dim = hidden_dim; p.vocab = vocab;
+    p.num_labels = num_labels; p.k = k;
+    return SLM_LAUNCH(ctx, slm::launch_label_head(p, ctx->stream), "label_head");
 }
 
 slm_status slm_beam_decode_attn(slm_ctx* ctx, const slm_beam_attn_args* a) {

@@ -158,6 +158,33 @@ typedef struct {
 slm_status slm_beam_decode_attn(slm_ctx *ctx, const slm_beam_attn_args *args);
 
 /*
+ * Prefill-only label head (§1.1, prefill-only models: after one prefill, the
+ * next-token logits at each sequence's last valid token are read at the
+ * target-label tokens only and turned into the business output by softmax,
+ * top-K or a fixed mapping).
+ *   hidden [T, H] bf16, cu_seqlens [B + 1] int32, lm_head [V, H] bf16 (only
+ *   the label rows are read), labels [L] int32 token ids, label_map [L]
+ *   int32 or NULL (device)
+ *   logits, probs [B, L] fp32 (probs may be NULL); top_idx [B, K] int32,
+ *   top_prob [B, K] fp32, top_class [B, K] int32 or NULL
+ * For sequence b: h = hidden[cu[b+1] - 1] (a zero row if the sequence is
+ * empty); logits[b, j] = h . lm_head[labels[j]] (bf16 products, fp32
+ * accumulation, a fixed summation order); probs[b, :] = softmax over the L
+ * label logits; top_idx[b, :] = the K labels with the largest logits,
+ * largest first, the lower index first among equal logits; top_prob their
+ * probabilities; top_class = label_map[top_idx] (= top_idx without a map).
+ * Needs H % 16 == 0, 1 <= K <= L, L <= 4096, K <= 64; hidden and lm_head
+ * 16-byte aligned.  Outputs must not overlap the inputs or each other.  A
+ * label id outside [0, V) or an invalid cu_seqlens sets the device error
+ * flag (SLM_ERR_INVALID_ARG at the next check); such a label reads row 0.
+ */
+slm_status slm_label_head(slm_ctx *ctx, const uint16_t *hidden, const int32_t *cu_seqlens,
+                          int32_t num_seqs, int32_t total_tokens, int32_t hidden_dim,
+                          const uint16_t *lm_head, int32_t vocab, const int32_t *labels,
+                          int32_t num_labels, int32_t k, const int32_t *label_map, float *logits,
+                          float *probs, int32_t *top_idx, float *top_prob, int32_t *top_class);
+
+/*
  * Beam top-k merge (§1.1: each step takes local candidates from every beam's
  * token distribution, merges them with the cumulative scores and keeps a
  * fixed number; the first step starts from the prefill's log-probs).

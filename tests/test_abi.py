@@ -108,6 +108,28 @@ def test_topk_logits_validation(dry):
         dry.beam_topk_merge_logits(x, cum, 4, lse_out=torch.zeros((3, 2)))
 
 
+def test_label_head_validation(dry):
+    hidden, lm = _bf(10, 64), _bf(50, 64)
+    cu = torch.tensor([0, 3, 10], dtype=torch.int32)
+    labels = torch.arange(8, dtype=torch.int32)
+    assert _status(lambda: dry.label_head(hidden, cu, lm, labels, 3)) == slm.SLM_OK
+    assert _status(lambda: dry.label_head(hidden, cu, lm, labels, 3, label_map=labels.clone(), probs=False)) \
+        == slm.SLM_OK
+    assert _status(lambda: dry.label_head(hidden, cu, lm, labels, 9)) == slm.SLM_ERR_INVALID_ARG       # k > L
+    assert _status(lambda: dry.label_head(_bf(10, 40), cu, _bf(50, 40), labels, 3)) == slm.SLM_ERR_UNSUPPORTED
+    assert _status(lambda: dry.label_head(hidden, cu, lm, torch.zeros(5000, dtype=torch.int32), 3)) \
+        == slm.SLM_ERR_UNSUPPORTED                                    # more than 4096 labels
+    buf = torch.zeros(64, dtype=torch.float32)
+    lg = buf[:16].view(2, 8)
+    ti = buf[8:14].view(torch.int32).view(2, 3)                       # overlaps logits
+    out = (lg, None, ti, torch.zeros((2, 3)), torch.zeros((2, 3), dtype=torch.int32))
+    assert _status(lambda: dry.label_head(hidden, cu, lm, labels, 3, out=out)) == slm.SLM_ERR_ALIAS
+    lab_alias = buf[16:24].view(torch.int32)
+    out2 = (buf[16:32].view(2, 8), None, torch.zeros((2, 3), dtype=torch.int32), torch.zeros((2, 3)),
+            torch.zeros((2, 3), dtype=torch.int32))
+    assert _status(lambda: dry.label_head(hidden, cu, lm, lab_alias, 3, out=out2)) == slm.SLM_ERR_ALIAS
+
+
 def _beam_args(NL=2, R=2, W=3, P=5, S=4, Hq=4, Hkv=2, D=64):
     return dict(q=_bf(NL, R, W, Hq, D), prefix_k=_bf(NL, R, P, Hkv, D), prefix_v=_bf(NL, R, P, Hkv, D),
                 suffix_k_in=_bf(NL, R, W, S, Hkv, D), suffix_v_in=_bf(NL, R, W, S, Hkv, D),

@@ -31,6 +31,7 @@ import numpy as np
 TID_Q, TID_K, TID_V, TID_HIDDEN = 1, 2, 3, 4
 TID_PREFIX_K, TID_PREFIX_V, TID_K_NEW, TID_V_NEW, TID_LOGITS = 5, 6, 7, 8, 9
 TID_SUFFIX_K, TID_SUFFIX_V = 10, 11
+TID_LM_HEAD, TID_LABELS = 12, 13
 
 
 @dataclasses.dataclass(frozen=True)
@@ -186,6 +187,22 @@ def beam_logprobs(shape: BeamShape, step: int) -> np.ndarray:
     prefill's, one row per request (``[R,1,V]``), later steps ``[R,W,V]``."""
     win = 1 if step == 0 else shape.width
     return logprobs(shape.base_seed, (shape.num_requests, win, shape.vocab), step)
+
+
+# -- label head (prefill-only mode): synthetic LM-head rows and label ids -------
+LABEL_COUNT, LABEL_TOP_K = 64, 5
+
+
+def lm_head_rows(base: int, vocab: int, hidden_dim: int) -> np.ndarray:
+    """bf16 LM-head rows [V, H]: N(0,1) / sqrt(H), so a unit-variance hidden
+    row gives unit-variance logits."""
+    x = _rng(base, TID_LM_HEAD).standard_normal((vocab, hidden_dim), dtype=np.float32)
+    return f32_to_bf16_bits((x / np.float32(np.sqrt(hidden_dim))).astype(np.float32))
+
+
+def label_ids(base: int, vocab: int, n: int = LABEL_COUNT) -> np.ndarray:
+    """n distinct token ids in [0, vocab)."""
+    return _rng(base, TID_LABELS).choice(vocab, size=n, replace=False).astype(np.int32)
 
 
 # -- torch device backend (bench-scale inputs) -----------------------------------
