@@ -223,6 +223,32 @@ def extra_workloads(ctx, dev, ev, reps=5):
         {"workload": "R8 x W400, P480, 5 steps, 24 layers, Hq14/Hkv2/D64, V151936"}, **bl.summary(per))
     del bl
     torch.cuda.empty_cache()
+    # beam-search prompt prefill: R equal-length prompts packed, K/V kept in
+    # the layout decode reads ([R*P, Hkv, D] per layer is [R, P, Hkv, D])
+    for bs in (wl.BEAM_SHORT, wl.BEAM_LONG):
+        R, P, Hq, Hkv, D, NL = bs.num_requests, bs.prompt_len, bs.n_heads_q, bs.n_heads_kv, bs.head_dim, bs.n_layers
+        q = wl.torch_normal_bf16((R * P, Hq, D), (bs.base_seed, wl.TID_Q, 0, 0), dev)
+        k = wl.torch_normal_bf16((R * P, Hkv, D), (bs.base_seed, wl.TID_PREFIX_K, 0, 0), dev)
+        v = wl.torch_normal_bf16((R * P, Hkv, D), (bs.base_seed, wl.TID_PREFIX_V, 0, 0), dev)
+        cu = torch.arange(R + 1, dtype=torch.int32, device=dev) * P
+        out = torch.empty((R * P, Hq, D), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            ctx.packed_prefill_attn(q, k, v, cu, P, out=out)
+        times = []
+        for _ in range(reps * 4):
+            e0 = ev()
+            ctx.packed_prefill_attn(q, k, v, cu, P, out=out)
+            times.append((e0, ev()))
+        torch.cuda.synchronize()
+        ctx.check()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in times)[len(times) // 2]
+        pbytes, pflops = prefill_bytes_flops([P] * R, Hq, Hkv, D, 4)
+        res["prompt_prefill_" + bs.name] = {
+            "workload": "%d prompts x %d tokens packed, Hq%d/Hkv%d/D%d, fp32 out; K/V in decode's layout" % (
+                R, P, Hq, Hkv, D),
+            "us_per_layer_median": round(us, 1), "us_all_%d_layers" % NL: round(us * NL, 1),
+            "hbm_frac": round(pbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del q, k, v, out
     # the merge on logits (log-softmax folded in) at both beam shapes
     for bs in (wl.BEAM_SHORT, wl.BEAM_LONG):
         R, W, V = bs.num_requests, bs.width, bs.vocab
