@@ -83,9 +83,9 @@ def topk_bytes(R, Win, V, W):
 
 
 def cpu_baseline(pf, bs):
-    """The oracle on a bounded sample of the same workload, scaled to the whole
-    step: 1/4 of the prefill sequences (one layer), one layer of each decode
-    step, and 4 requests of each merge."""
+    """The oracle on a bounded sample of the same workload (roughly 10 s on 16
+    host threads), scaled to the whole step: one whole prefill layer (all 960
+    sequences), one layer of each decode step, and 8 requests of each merge."""
     import numpy as np
 
     import oracle
@@ -93,7 +93,7 @@ def cpu_baseline(pf, bs):
 
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     L = list(pf.lengths)
-    sub = L[::4]
+    sub = L
     shp = wl.PrefillShape("sample", pf.base_seed, tuple(sub), pf.n_heads_q, pf.n_heads_kv, pf.head_dim)
     x = wl.prefill_inputs(shp)
     t0 = time.perf_counter()
@@ -115,7 +115,7 @@ def cpu_baseline(pf, bs):
         t_dec += time.perf_counter() - t0
     est += t_dec * bs.n_layers
 
-    r_s = 4
+    r_s = 8
     t_top = 0.0
     for t in range(0, bs.n_steps + 1):
         win = 1 if t == 0 else bs.width
@@ -132,7 +132,7 @@ def cpu_baseline(pf, bs):
         "cores": threads,
         "kind": "oracle",
         "sample": ("fp64 C oracle, %d threads: prefill layer 0 over %d of 960 sequences (%d tokens), "
-                   "decode layer 0 of each of the 4 steps, top-k merge of 4 of 32 requests for the 5 merges; "
+                   "decode layer 0 of each of the 4 steps, top-k merge of 8 of 32 requests for the 5 merges; "
                    "%.1f s measured, scaled by causal pairs / layers / requests to one whole step "
                    "(%.0f s estimated)" % (threads, len(sub), sum(sub), sampled, est)),
     }
