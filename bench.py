@@ -258,21 +258,24 @@ def extra_workloads(ctx, dev, ev, reps=5):
         cum = torch.randn((R, W), generator=gc, device=dev) * 3 - 10
         outs = [torch.empty((R, W), dtype=torch.int32, device=dev), torch.empty((R, W), dtype=torch.int32, device=dev),
                 torch.empty((R, W), dtype=torch.float32, device=dev)]
-        for _ in range(3):
-            ctx.beam_topk_merge_logits(x, cum, W, *outs)
-        times = []
-        for _ in range(reps * 4):
-            e0 = ev()
-            ctx.beam_topk_merge_logits(x, cum, W, *outs)
-            times.append((e0, ev()))
-        torch.cuda.synchronize()
-        ctx.check()
-        us = sorted(a.elapsed_time(b) * 1e3 for a, b in times)[len(times) // 2]
-        nbytes = R * W * V * 4 + R * W * 4 + 3 * R * W * 4
-        res["merge_on_logits_" + bs.name] = {
-            "workload": "R%d x Win%d x V%d fp32 logits -> top %d (row log-sum-exp folded in)" % (R, W, V, W),
-            "us_median": round(us, 1), "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "bytes": nbytes}
+        for xx, tag, eb in ((x, "", 4), (x.to(torch.bfloat16), "_bf16", 2)):
+            for _ in range(3):
+                ctx.beam_topk_merge_logits(xx, cum, W, *outs)
+            times = []
+            for _ in range(reps * 4):
+                e0 = ev()
+                ctx.beam_topk_merge_logits(xx, cum, W, *outs)
+                times.append((e0, ev()))
+            torch.cuda.synchronize()
+            ctx.check()
+            us = sorted(a.elapsed_time(b) * 1e3 for a, b in times)[len(times) // 2]
+            nbytes = R * W * V * eb + R * W * 4 + 3 * R * W * 4
+            res["merge_on_logits_" + bs.name + tag] = {
+                "workload": "R%d x Win%d x V%d %s logits -> top %d (row log-sum-exp folded in)" % (
+                    R, W, V, "bf16" if eb == 2 else "fp32", W),
+                "us_median": round(us, 1), "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "bytes": nbytes}
+            del xx
         del x
     torch.cuda.empty_cache()
     return {"reporting_only": res}

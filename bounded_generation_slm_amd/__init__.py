@@ -72,7 +72,7 @@ _lib.slm_packed_prefill_attn.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
 _lib.slm_gather_last.argtypes = [_P, _P, _P, _I, _I, _I, ctypes.c_int, _P]
 _lib.slm_beam_decode_attn.argtypes = [_P, ctypes.POINTER(_BeamAttnArgs)]
 _lib.slm_beam_topk_merge.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]
-_lib.slm_beam_topk_merge_logits.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P]
+_lib.slm_beam_topk_merge_logits.argtypes = [_P, _P, ctypes.c_int, _P, _I, _I, _I, _I, _P, _P, _P, _P]
 _lib.slm_label_head.argtypes = [_P, _P, _P, _I, _I, _I, _P, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P]
 _lib.slm_beam_reorder_suffix.argtypes = [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
 for _name in ("slm_ctx_create", "slm_ctx_set_stream", "slm_ctx_check", "slm_packed_prefill_attn",
@@ -298,8 +298,8 @@ def slm_beam_topk_merge(ctx: Context, logprobs, cum, width: int, tokens=None, pa
 
 def slm_beam_topk_merge_logits(ctx: Context, logits, cum, width: int, tokens=None, parent=None, cum_out=None,
                                lse_out=None):
-    """logits [R,Win,V] fp32, cum [R,Win] fp32 -> (tokens, parent, cum_out) [R,W]; lse_out [R,Win]
-    fp32 (optional) receives each row's log-sum-exp."""
+    """logits [R,Win,V] fp32 or bf16, cum [R,Win] fp32 -> (tokens, parent, cum_out) [R,W]; lse_out
+    [R,Win] fp32 (optional) receives each row's log-sum-exp."""
     dev = ctx.device
     R, Win, V = logits.shape
     if tuple(cum.shape) != (R, Win):
@@ -315,7 +315,8 @@ def slm_beam_topk_merge_logits(ctx: Context, logits, cum, width: int, tokens=Non
             raise ValueError("%s must be [R, W]" % name)
     ctx._stream()
     rc = _lib.slm_beam_topk_merge_logits(
-        ctx._h, _ptr(logits, "logits", (torch.float32,), dev), _ptr(cum, "cum", (torch.float32,), dev),
+        ctx._h, _ptr(logits, "logits", (torch.float32, torch.bfloat16), dev),
+        SLM_BF16 if logits.dtype == torch.bfloat16 else SLM_F32, _ptr(cum, "cum", (torch.float32,), dev),
         R, Win, V, W, _ptr(tokens, "tokens", (torch.int32,), dev), _ptr(parent, "parent", (torch.int32,), dev),
         _ptr(cum_out, "cum_out", (torch.float32,), dev),
         None if lse_out is None else _ptr(lse_out, "lse_out", (torch.float32,), dev))

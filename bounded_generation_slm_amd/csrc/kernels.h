@@ -132,6 +132,7 @@ struct TopkParams {
     int rows_per_chunk, chunks;         // first-level chunks of beam rows per request
     int level2_w;                       // key slots per chunk in level2 (max_beams)
     int* err;                           // device error flag
+    bool logits_bf16;                   // merge on logits: bf16 logits (else fp32)
 };
 constexpr int kTopkLogitChunks = 64;    // first-level chunks per request at most
 constexpr int kTopkChunkPieces = 512;   // pieces per first-level chunk at most

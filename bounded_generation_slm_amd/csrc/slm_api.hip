@@ -438,9 +438,9 @@ slm_status slm_beam_topk_merge(slm_ctx* ctx, const float* logprobs, const float*
     return SLM_LAUNCH(ctx, slm::launch_beam_topk_merge(p, ctx->stream), "topk");
 }
 
-slm_status slm_beam_topk_merge_logits(slm_ctx* ctx, const float* logits, const float* cum, int32_t num_requests,
-                                      int32_t beams_in, int32_t vocab, int32_t width, int32_t* tokens,
-                                      int32_t* parent, float* cum_out, float* lse_out) {
+slm_status slm_beam_topk_merge_logits(slm_ctx* ctx, const void* logits, slm_dtype logits_dtype, const float* cum,
+                                      int32_t num_requests, int32_t beams_in, int32_t vocab, int32_t width,
+                                      int32_t* tokens, int32_t* parent, float* cum_out, float* lse_out) {
     slm_status s = enter(ctx);
     if (s != SLM_OK) return s;
     if (num_requests < 0 || beams_in <= 0 || vocab <= 0 || width <= 0)
@@ -455,14 +455,17 @@ slm_status slm_beam_topk_merge_logits(slm_ctx* ctx, const float* logits, const f
         vocab > ctx->caps.max_vocab)
         return fail(ctx, SLM_ERR_CAPACITY, "topk_logits: beyond the context caps (requests %d, beams %d, vocab %d)",
                     ctx->caps.max_requests, ctx->caps.max_beams, ctx->caps.max_vocab);
+    if (logits_dtype != SLM_F32 && logits_dtype != SLM_BF16)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "topk_logits: logits must be fp32 or bf16");
     if (num_requests == 0) return ok(ctx);
     if (!logits || !cum || !tokens || !parent || !cum_out)
         return fail(ctx, SLM_ERR_INVALID_ARG, "topk_logits: NULL tensor");
-    if (((uintptr_t)logits & 3) || ((uintptr_t)cum & 3) || ((uintptr_t)tokens & 3) || ((uintptr_t)parent & 3) ||
+    const size_t xe = logits_dtype == SLM_BF16 ? 2 : 4;
+    if (((uintptr_t)logits & (xe - 1)) || ((uintptr_t)cum & 3) || ((uintptr_t)tokens & 3) || ((uintptr_t)parent & 3) ||
         ((uintptr_t)cum_out & 3) || ((uintptr_t)lse_out & 3))
-        return fail(ctx, SLM_ERR_INVALID_ARG, "topk_logits: tensors must be 4-byte aligned");
+        return fail(ctx, SLM_ERR_INVALID_ARG, "topk_logits: misaligned tensor");
     const size_t R = num_requests;
-    const size_t xb = R * beams_in * (size_t)vocab * 4, cb = R * beams_in * 4, ob = R * width * 4;
+    const size_t xb = R * beams_in * (size_t)vocab * xe, cb = R * beams_in * 4, ob = R * width * 4;
     const void* outs[] = {tokens, parent, cum_out};
     for (const void* o : outs)
         if (overlaps(o, ob, logits, xb) || overlaps(o, ob, cum, cb))
@@ -476,8 +479,9 @@ slm_status slm_beam_topk_merge_logits(slm_ctx* ctx, const float* logits, const f
             if (overlaps(lse_out, cb, o, ob)) return fail(ctx, SLM_ERR_ALIAS, "topk_logits: lse_out overlaps an output");
     }
     slm::TopkParams p{};
-    p.logprobs = logits; p.cum = cum; p.tokens = tokens; p.parent = parent; p.cum_out = cum_out;
+    p.logprobs = (const float*)logits; p.cum = cum; p.tokens = tokens; p.parent = parent; p.cum_out = cum_out;
     p.lse_out = lse_out;
+    p.logits_bf16 = logits_dtype == SLM_BF16;
     p.err = ctx->err_flag;
     const int64_t R_cap = ctx->caps.max_requests;
     p.req_state = ctx->topk_ws;

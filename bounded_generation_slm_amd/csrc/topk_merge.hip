@@ -28,6 +28,7 @@
 // it and raises the threshold to it, so later candidates are rejected with
 // one compare.  Insertion compacts each wave's survivors with ballots.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -723,7 +724,9 @@ __device__ __forceinline__ int64_t part_slot(int64_t wid, int64_t row, int64_t s
     return wid * rpw + (row - wid * seg / V);
 }
 
-template <bool VEC>
+// BF16: the logits are bf16 (8 per 16-byte load; lane l of a round holds
+// elements 8l .. 8l + 7), else fp32 (two 16-byte loads of 4, at 4l and 256 + 4l).
+template <bool VEC, bool BF16>
 __global__ __launch_bounds__(kTkThreads) void topk_logits_stage1_kernel(const TopkParams p) {
     extern __shared__ __attribute__((aligned(16))) uint64_t wave_lds[];
     const int lane = threadIdx.x & 63;
@@ -740,14 +743,18 @@ __global__ __launch_bounds__(kTkThreads) void topk_logits_stage1_kernel(const To
     uint64_t* surv = buf + soft + kWRound;
     int* hist = (int*)(surv + ((W + 1) & ~1));
 
-    constexpr int NV = kWPerLane / 4;
-    constexpr int LPF = VEC ? NV : kWPerLane;                   // load instructions per round
+    constexpr int NV = BF16 ? 1 : kWPerLane / 4;               // 16-byte registers per round
+    // element k (0..7) of this lane in round rd
+    auto elem = [&](int rd, int k) {
+        return BF16 ? rd * kWRound + lane * 8 + k : rd * kWRound + ((k >> 2) * kWLanes + lane) * 4 + (k & 3);
+    };
     while (a < end) {
         const int64_t row = a / V;                              // r * Win + b
         const int r = (int)(row / p.beams_in);
         const int64_t pe = min(end, (row + 1) * V);             // this piece: [a, pe) inside one row
         const int n = (int)(pe - a);
         const float* xp = p.logprobs + a;
+        const uint16_t* xh = (const uint16_t*)p.logprobs + a;    // BF16
         const uint32_t f0 = (uint32_t)(a - (int64_t)r * req_len);   // flat index b*V + v of xp[0]
         const int rounds = (n + kWRound - 1) / kWRound;
         uint64_t thr = 0;                                       // keys > thr pass (this piece only)
@@ -759,29 +766,45 @@ __global__ __launch_bounds__(kTkThreads) void topk_logits_stage1_kernel(const To
             thr = own > thr ? own : thr;
             wave_fence();
         };
-        f32x4 B0[NV], B1[NV], B2[NV], B3[NV];
-        auto fetch = [&](int rd, f32x4 (&dst)[NV]) {
-#pragma unroll
-            for (int j = 0; j < NV; ++j) {
-                const int i0 = rd * kWRound + (j * kWLanes + lane) * 4;
+        using Buf = std::conditional_t<BF16, u32x4, f32x4>;     // one round: 8 bf16 bit pairs, or 2 x 4 fp32
+        Buf B0[NV], B1[NV], B2[NV], B3[NV];
+        auto fetch = [&](int rd, Buf (&dst)[NV]) {
+            if constexpr (BF16) {
+                const int i0 = elem(rd, 0);
                 if (VEC) {
-                    dst[j] = stream_load16(xp + min(i0, n - 4));
+                    dst[0] = __builtin_nontemporal_load((const u32x4*)(xh + min(i0, n - 8)));
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) dst[j][e] = stream_load4(xp + min(i0 + e, n - 1));
+                    for (int e = 0; e < 4; ++e)
+                        dst[0][e] = (uint32_t)__builtin_nontemporal_load(xh + min(i0 + 2 * e, n - 1)) |
+                                    ((uint32_t)__builtin_nontemporal_load(xh + min(i0 + 2 * e + 1, n - 1)) << 16);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NV; ++j) {
+                    const int i0 = elem(rd, 4 * j);
+                    if (VEC) {
+                        dst[j] = stream_load16(xp + min(i0, n - 4));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) dst[j][e] = stream_load4(xp + min(i0 + e, n - 1));
+                    }
                 }
             }
         };
-        auto round = [&](int rd, f32x4 (&src)[NV]) {
+        auto round = [&](int rd, Buf (&src)[NV]) {
             float x[kWPerLane];
             bool valid[kWPerLane];
 #pragma unroll
-            for (int j = 0; j < NV; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[j * 4 + e] = src[j][e];
-                    valid[j * 4 + e] = rd * kWRound + (j * kWLanes + lane) * 4 + e < n;
+            for (int k = 0; k < kWPerLane; ++k) {
+                if constexpr (BF16) {
+                    const uint32_t w2 = src[0][k >> 1];
+                    x[k] = bf16_bits_to_f32((k & 1) ? (w2 >> 16) : (w2 & 0xFFFFu));
+                } else {
+                    x[k] = src[k >> 2][k & 3];
                 }
+                valid[k] = elem(rd, k) < n;
+            }
             // the row's normaliser: clamped re-reads are logits of this piece
             // too, so they may join the max but not the sum
             float rmax = x[0];
@@ -808,13 +831,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_logits_stage1_kernel(const To
             for (int k = 0; k < kWPerLane; ++k) maybe |= x[k] >= ts;
             if (__ballot(maybe) == 0) return;
 #pragma unroll
-            for (int j = 0; j < NV; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool ok = x[j * 4 + e] >= ts;
+            for (int k = 0; k < kWPerLane; ++k) {
+                    const bool ok = x[k] >= ts;
                     if (__ballot(ok) == 0) continue;
-                    const int i = rd * kWRound + (j * kWLanes + lane) * 4 + e;
-                    const uint64_t key = (ok && i < n) ? make_key(x[j * 4 + e], f0 + (uint32_t)i) : 0ull;
+                    const int i = elem(rd, k);
+                    const uint64_t key = (ok && i < n) ? make_key(x[k], f0 + (uint32_t)i) : 0ull;
                     const bool pass = key > thr;
                     const uint64_t m = __ballot(pass);
                     if (pass) buf[cnt + lanes_below(m)] = key;
@@ -1076,7 +1097,7 @@ int64_t beam_topk_logits_segment(int num_requests, int beams_in, int vocab, int6
     // it, and each of its beams_in - 1 inner row boundaries splits one more
     const int64_t free_slots = std::max<int64_t>(1, lists - beams_in - 1);
     seg = std::max<int64_t>(seg, (req_len + free_slots - 1) / free_slots);
-    seg = (seg + 3) & ~(int64_t)3;
+    seg = (seg + 7) & ~(int64_t)7;                              // whole 16-byte loads of fp32 or bf16
     for (;;) {
         const int64_t waves = (total + seg - 1) / seg;
         const int64_t per = (seg - 1) / vocab + 2;              // rows one range can touch
@@ -1095,22 +1116,32 @@ int64_t beam_topk_logits_segment(int num_requests, int beams_in, int vocab, int6
             chunks = (int)((beams_in + rpc - 1) / rpc);
             return seg;
         }
-        seg = (2 * seg + 3) & ~(int64_t)3;
+        seg = (2 * seg + 7) & ~(int64_t)7;
     }
 }
 
 hipError_t launch_beam_topk_merge_logits(const TopkParams& p, hipStream_t stream) {
     if (p.num_requests == 0) return hipSuccess;
-    const bool vec = (p.vocab % 4 == 0) && (((uintptr_t)p.logprobs & 15) == 0);
+    const bool vec = (p.vocab % (p.logits_bf16 ? 8 : 4) == 0) && (p.seg % 8 == 0) && (((uintptr_t)p.logprobs & 15) == 0);
     const int64_t total = (int64_t)p.num_requests * p.beams_in * p.vocab;
     const int64_t waves = (total + p.seg - 1) / p.seg;
     const int64_t blocks = (waves + kTkThreads / kWLanes - 1) / (kTkThreads / kWLanes);
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const size_t lds = beam_topk_stage1_lds(p.width);
-    if (vec)
-        hipLaunchKernelGGL(topk_logits_stage1_kernel<true>, dim3((unsigned)blocks), dim3(kTkThreads), lds, stream, p);
-    else
-        hipLaunchKernelGGL(topk_logits_stage1_kernel<false>, dim3((unsigned)blocks), dim3(kTkThreads), lds, stream, p);
+    if (p.logits_bf16) {
+        if (vec)
+            hipLaunchKernelGGL((topk_logits_stage1_kernel<true, true>), dim3((unsigned)blocks), dim3(kTkThreads), lds,
+                               stream, p);
+        else
+            hipLaunchKernelGGL((topk_logits_stage1_kernel<false, true>), dim3((unsigned)blocks), dim3(kTkThreads), lds,
+                               stream, p);
+    } else if (vec) {
+        hipLaunchKernelGGL((topk_logits_stage1_kernel<true, false>), dim3((unsigned)blocks), dim3(kTkThreads), lds,
+                           stream, p);
+    } else {
+        hipLaunchKernelGGL((topk_logits_stage1_kernel<false, false>), dim3((unsigned)blocks), dim3(kTkThreads), lds,
+                           stream, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_logits_chunk_kernel, dim3(p.chunks, p.num_requests), dim3(kTkThreads), 0, stream, p);
@@ -1129,7 +1160,7 @@ hipError_t launch_beam_topk_merge_logits(const TopkParams& p, hipStream_t stream
 int beam_topk_logits_blocks_per_cu(int width) {
     int n = 0;
     const size_t lds = beam_topk_stage1_lds(width);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)topk_logits_stage1_kernel<true>, kTkThreads,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)topk_logits_stage1_kernel<true, false>, kTkThreads,
                                                      lds) != hipSuccess ||
         n <= 0)
         n = 1;

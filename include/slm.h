@@ -209,9 +209,11 @@ slm_status slm_beam_topk_merge(slm_ctx *ctx, const float *logprobs, const float 
  * log-softmax folded in, so the log-probabilities are never written (§1.1:
  * the fixed beam-search node takes the model's output straight into the
  * merge).
- *   logits [R, Win, V] fp32, cum [R, Win] fp32 (device)
+ *   logits [R, Win, V] fp32 or bf16 (logits_dtype), cum [R, Win] fp32 (device)
  *   tokens, parent [R, W] int32; cum_out [R, W] fp32; lse_out [R, Win] fp32
  *   or NULL (each row's log-sum-exp, for inspection)
+ * bf16 logits are widened exactly to fp32 and then treated as fp32 ones (half
+ * the bytes read).
  * For row (r, b): lse = log sum_v exp(logits[r,b,v]), computed in fp32 from
  * the row's maximum (approximate: exp and log by the hardware's fp32
  * instructions, partial sums combined in a fixed order, so repeated calls
@@ -225,9 +227,9 @@ slm_status slm_beam_topk_merge(slm_ctx *ctx, const float *logprobs, const float 
  * Outputs must not overlap the inputs or each other.  The logits are read
  * once (one HBM pass); the call allocates nothing.
  */
-slm_status slm_beam_topk_merge_logits(slm_ctx *ctx, const float *logits, const float *cum,
-                                      int32_t num_requests, int32_t beams_in, int32_t vocab,
-                                      int32_t width, int32_t *tokens, int32_t *parent,
+slm_status slm_beam_topk_merge_logits(slm_ctx *ctx, const void *logits, slm_dtype logits_dtype,
+                                      const float *cum, int32_t num_requests, int32_t beams_in,
+                                      int32_t vocab, int32_t width, int32_t *tokens, int32_t *parent,
                                       float *cum_out, float *lse_out);
 
 /*

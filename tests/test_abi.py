@@ -106,6 +106,9 @@ def test_topk_logits_validation(dry):
         == slm.SLM_ERR_ALIAS                                        # lse_out overlaps cum
     with pytest.raises(ValueError):
         dry.beam_topk_merge_logits(x, cum, 4, lse_out=torch.zeros((3, 2)))
+    assert _status(lambda: dry.beam_topk_merge_logits(x.to(torch.bfloat16), cum, 4)) == slm.SLM_OK
+    with pytest.raises(TypeError):
+        dry.beam_topk_merge_logits(x.half(), cum, 4)
 
 
 def test_label_head_validation(dry):

@@ -110,6 +110,20 @@ def test_quantised_ties(gpu):
                 assert tok[r, j] < tok[r, j + 1]
 
 
+@pytest.mark.parametrize("R,Win,V,W", [(2, 4, 1000, 4), (3, 5, 1003, 17), (4, 1, 151936, 100), (3, 7, 2048, 512)])
+def test_bf16_logits(gpu, R, Win, V, W):
+    """bf16 logits: widened exactly, then the same definition (the oracle gets
+    the widened values)."""
+    note("topk_logits bf16 R=%d Win=%d V=%d W=%d" % (R, Win, V, W))
+    rng = np.random.default_rng(R * 31 + V + W)
+    bits = wl.f32_to_bf16_bits((rng.standard_normal((R, Win, V)) * 3).astype(np.float32))
+    x = wl.bf16_bits_to_f32(bits)
+    cum = (rng.standard_normal((R, Win)) * 2 - 5).astype(np.float32)
+    xd = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    got = _run(gpu, xd, torch.from_numpy(cum).cuda(), W)
+    _check(got, x, cum, W, "bf16")
+
+
 @pytest.mark.parametrize("shape", [wl.BEAM_SHORT, wl.BEAM_LONG], ids=lambda s: s.name)
 def test_full_size(gpu, shape):
     """The merge at the workload's full size (151,936-word vocabulary, the
@@ -126,3 +140,16 @@ def test_full_size(gpu, shape):
         assert np.array_equal(a, b), "two launches differ"
     exact = _check(got, x.cpu().numpy(), cum.numpy(), W, shape.name)
     note("topk_logits %s: %d of %d requests exact (the rest have oracle near-ties)" % (shape.name, exact, R))
+
+
+
+def test_full_size_bf16(gpu):
+    """bf16 logits at the short-prompt shape's full size."""
+    shape = wl.BEAM_SHORT
+    note("topk_logits %s full size, bf16 logits" % shape.name)
+    R, W, V = shape.num_requests, shape.width, shape.vocab
+    x = wl.torch_logits((R, W, V), (shape.base_seed, wl.TID_LOGITS, 0, 2), "cuda").to(torch.bfloat16)
+    g = torch.Generator().manual_seed(4)
+    cum = (torch.randn((R, W), generator=g) * 3 - 10).float()
+    got = _run(gpu, x, cum.cuda(), W)
+    _check(got, x.float().cpu().numpy(), cum.numpy(), W, "bf16 full size")
