@@ -82,6 +82,31 @@ def topk_bytes(R, Win, V, W):
     return R * Win * V * 4 + R * Win * 4 + R * W * 12
 
 
+def one_thread_times():
+    """The oracle with one OpenMP thread on the tiny config's prefill and merge
+    and the one-request prefill (15 sequences), in a child process (the thread
+    count of a running OpenMP runtime cannot be changed from here)."""
+    import subprocess
+    code = (
+        "import time, numpy as np, oracle, workloads as wl\n"
+        "res = {}\n"
+        "for name, shp in (('tiny_prefill', wl.TINY_PREFILL), ('prefill_request', wl.PREFILL_REQUEST)):\n"
+        "    x = wl.prefill_inputs(shp); t0 = time.perf_counter()\n"
+        "    oracle.prefill_attn(x['q'], x['k'], x['v'], x['cu_seqlens']); res[name] = time.perf_counter() - t0\n"
+        "s = wl.TINY_BEAM; lp = wl.beam_logprobs(s, 1); t0 = time.perf_counter()\n"
+        "oracle.topk_merge(lp, np.zeros((s.num_requests, s.width), np.float32), s.width)\n"
+        "res['tiny_merge'] = time.perf_counter() - t0\n"
+        "print(repr({k: round(v, 4) for k, v in res.items()}))\n")
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    try:
+        out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT,
+                             timeout=120)
+        import ast
+        return ast.literal_eval(out.stdout.strip().splitlines()[-1])
+    except Exception as e:                                      # reporting only
+        return {"error": str(e)[:200]}
+
+
 def cpu_baseline(pf, bs):
     """The oracle on a bounded sample of the same workload (roughly 10 s on 16
     host threads), scaled to the whole step: one whole prefill layer (all 960
@@ -126,11 +151,22 @@ def cpu_baseline(pf, bs):
         t_top += time.perf_counter() - t0
     est += t_top * bs.num_requests / r_s
     sampled = t_pre + t_dec + t_top
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": pf.total_tokens / est,
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
+        "host": {"cpu_model": cpu_model, "logical_cpus": os.cpu_count(), "omp_threads": threads,
+                 "one_thread_s": one_thread_times()},
         "sample": ("fp64 C oracle, %d threads: prefill layer 0 over %d of 960 sequences (%d tokens), "
                    "decode layer 0 of each of the 4 steps, top-k merge of 8 of 32 requests for the 5 merges; "
                    "%.1f s measured, scaled by causal pairs / layers / requests to one whole step "
@@ -355,6 +391,7 @@ class BeamRun:
                                for t in range(1, N + 1)],
             "reorder_us": round(avg["reorder"], 1),
             "beam_requests_per_s": round(R / (search_us * 1e-6), 1),
+            "beams_steps_per_s": round(R * W * N / (sum(step_us) * 1e-6), 1),
         }
 
 
