@@ -27,6 +27,11 @@ namespace slm {
 namespace {
 
 constexpr size_t kDecSmallLds = 80 * 1024;     // two workgroups per CU fit
+// fp32 output staged per wave through LDS, one 32-column half of the 32-row
+// block at a time (row pitch 36 floats: the 16-byte writes of 16 lanes and
+// the 16-byte reads of 16 lanes each cover all 64 banks once)
+constexpr int kStageRow = 36;
+constexpr size_t kStageWaveBytes = 32 * kStageRow * sizeof(float);
 
 template <int D>
 struct DecodeLds {
@@ -38,7 +43,10 @@ struct DecodeLds {
     }
 };
 
-template <int D, bool OUT_BF16, int NTHR>
+// STAGE: the fp32 output leaves through a per-wave LDS tile, so each store
+// instruction writes whole 128-byte row halves (eight rows) instead of 32-byte
+// pieces of 32 rows.
+template <int D, bool OUT_BF16, int NTHR, bool STAGE>
 __global__ __launch_bounds__(NTHR) void beam_decode_attn_kernel(const DecodeParams p,
                                                                           int chunks, int chunk_rows) {
     constexpr int NKS = D / 16, NDB = D / 32, KROW = D + 8;
@@ -48,6 +56,7 @@ __global__ __launch_bounds__(NTHR) void beam_decode_attn_kernel(const DecodePara
     const int VROW = DecodeLds<D>::vrow(P);
     uint16_t* k_lds = lds;                        // [PP][KROW]
     uint16_t* vt_lds = lds + (size_t)PP * KROW;   // [D][VROW], keys permuted per 16
+    static_assert(!STAGE || !OUT_BF16, "the staged epilogue writes fp32");
 
     const int R = p.num_requests, W = p.width, G = p.group, Hkv = p.n_heads_kv;
     const int n_units = p.n_layers * R * Hkv;
@@ -271,7 +280,31 @@ __global__ __launch_bounds__(NTHR) void beam_decode_attn_kernel(const DecodePara
         }
 
         lsum += __shfl_xor(lsum, 32);
-        if (valid) {
+        if constexpr (STAGE) {
+            // tile [32 rows][kStageRow] floats behind the prompt copy, one per wave
+            float* st = (float*)(vt_lds + (size_t)D * VROW) + (size_t)wave * 32 * kStageRow;
+            const float inv = valid ? 1.f / lsum : 0.f;
+            const int c = lane >> 3, rr = lane & 7;   // read side: 16-byte chunk c of row 8k + rr
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4)
+                    *(f32x4*)(st + n * kStageRow + 8 * i4 + 4 * hf) =
+                        f32x4{o[db][4 * i4] * inv, o[db][4 * i4 + 1] * inv, o[db][4 * i4 + 2] * inv,
+                              o[db][4 * i4 + 3] * inv};
+                __builtin_amdgcn_wave_barrier();      // LDS is in order within a wave
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int row = 8 * k + rr, m2 = blk + row;
+                    const f32x4 x = *(const f32x4*)(st + row * kStageRow + 4 * c);
+                    if (m2 < row1) {
+                        const int64_t qo2 = (((int64_t)lr * W + m2 / G) * p.n_heads_q + g * G + m2 % G) * D;
+                        __builtin_nontemporal_store(x, (f32x4*)((float*)p.out + qo2 + db * 32 + 4 * c));
+                    }
+                }
+                __builtin_amdgcn_wave_barrier();      // reads of this half before the next half's writes
+            }
+        } else if (valid) {
             const float inv = 1.f / lsum;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -291,7 +324,7 @@ __global__ __launch_bounds__(NTHR) void beam_decode_attn_kernel(const DecodePara
     }
 }
 
-template <int D, bool OUT_BF16, int NTHR>
+template <int D, bool OUT_BF16, int NTHR, bool STAGE>
 hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
     const int n_units = p.n_layers * p.num_requests * p.n_heads_kv;
     const int M = p.width * p.group;
@@ -304,8 +337,8 @@ hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
     const int64_t units_padded = ((int64_t)n_units + kNumXcd - 1) / kNumXcd * kNumXcd;
     const int64_t blocks = units_padded * chunks;
     if (blocks == 0) return hipSuccess;
-    const size_t lds = DecodeLds<D>::bytes(p.prompt_len);
-    auto kern = beam_decode_attn_kernel<D, OUT_BF16, NTHR>;
+    const size_t lds = DecodeLds<D>::bytes(p.prompt_len) + (STAGE ? (NTHR / kWave) * kStageWaveBytes : 0);
+    auto kern = beam_decode_attn_kernel<D, OUT_BF16, NTHR, STAGE>;
     // raise the kernel's dynamic-LDS limit only when a call needs more than
     // before (no host call per launch, so launches can be graph-captured);
     // the lock keeps the recorded limit and the attribute in step across threads
@@ -333,11 +366,18 @@ hipError_t launch_beam_decode_attn(const DecodeParams& p, int head_dim, bool out
                                    hipStream_t stream) {
     // A prompt copy too large for two workgroups per CU is shared by 16 waves
     // (head_dim 64; at 128 the registers of 16 waves would not hold a lane's state).
-    const bool wide = head_dim == 64 && beam_decode_lds_bytes(head_dim, p.prompt_len) > kDecSmallLds;
+    // The fp32 output is staged through LDS where the tiles still leave room
+    // for two workgroups per CU.
+    const size_t prompt_lds = beam_decode_lds_bytes(head_dim, p.prompt_len);
+    const bool wide = head_dim == 64 && prompt_lds > kDecSmallLds;
+    const bool stage = head_dim == 64 && !out_bf16 && prompt_lds + 8 * kStageWaveBytes <= kDecSmallLds;
     if (head_dim == 128)
-        return out_bf16 ? launch_variant<128, true, 512>(p, stream) : launch_variant<128, false, 512>(p, stream);
-    return out_bf16 ? (wide ? launch_variant<64, true, 1024>(p, stream) : launch_variant<64, true, 512>(p, stream))
-                    : (wide ? launch_variant<64, false, 1024>(p, stream) : launch_variant<64, false, 512>(p, stream));
+        return out_bf16 ? launch_variant<128, true, 512, false>(p, stream)
+                        : launch_variant<128, false, 512, false>(p, stream);
+    if (out_bf16)
+        return wide ? launch_variant<64, true, 1024, false>(p, stream) : launch_variant<64, true, 512, false>(p, stream);
+    if (stage) return launch_variant<64, false, 512, true>(p, stream);
+    return wide ? launch_variant<64, false, 1024, false>(p, stream) : launch_variant<64, false, 512, false>(p, stream);
 }
 
 }  // namespace slm

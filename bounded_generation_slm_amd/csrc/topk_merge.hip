@@ -286,24 +286,28 @@ __device__ __forceinline__ uint64_t* req_slot(const TopkParams& p, int r, int s)
 
 // ---- stage 1: one wave per (request, beam row, vocabulary chunk) ----
 //
-// Each wave owns a private LDS region (candidate buffer, survivor area, 256
-// radix bins); its candidate count and threshold live in wave-uniform
-// registers, so the streaming loop has no workgroup barrier and no LDS
-// atomic.  Loads are unconditional (addresses clamped into the chunk, values
-// masked afterwards) and rotate through four register buffers, four rounds in
-// flight.  A candidate is first screened on its fp32 score alone; the 64-bit
-// key is built only in the rare rounds where a lane passes.
+// Each wave owns a private LDS region (candidate buffer and 256 radix bins);
+// its candidate count and threshold live in wave-uniform registers, so the
+// streaming loop has no workgroup barrier and no LDS atomic.  Loads are
+// unconditional (addresses clamped into the chunk, values masked afterwards)
+// and rotate through four register buffers, four rounds in flight.  A
+// candidate is first screened on its fp32 score alone; the 64-bit key is
+// built only in the rare rounds where a lane passes.
 constexpr int kWLanes = 64;
 constexpr int kWPerLane = 8;                        // candidates per lane per round
 constexpr int kWRound = kWLanes * kWPerLane;        // 512
 constexpr int kWDepth = 4;                          // rounds in flight
 constexpr int kWBins = 256;
 
-// LDS layout of one wave, in 8-byte words: buf[soft + kWRound], surv[even(W)],
-// hist[kWBins] ints.
-__host__ __device__ inline int wave_soft_cap(int W) { return W > 512 ? 2 * W : 512; }
+// LDS layout of one wave, in 8-byte words: buf[soft + kWRound], hist[kWBins]
+// ints.  Widths above 256 get no first-round bound and would compact every
+// round or two while their own threshold is still loose, so their buffer
+// keeps a round's worth of slots (512) free after a compaction; narrower
+// ones compact at 512 keys, which raises their threshold sooner.  Four
+// workgroups fit a CU up to W = 256, three up to W = 512.
+__host__ __device__ inline int wave_soft_cap(int W) { return W > kWRound / 2 ? W + kWRound : kWRound; }
 __host__ __device__ inline int wave_lds_words(int W) {
-    return wave_soft_cap(W) + kWRound + ((W + 1) & ~1) + kWBins / 2;
+    return wave_soft_cap(W) + kWRound + kWBins / 2;
 }
 
 __device__ __forceinline__ void wave_fence() { __builtin_amdgcn_wave_barrier(); }
@@ -407,8 +411,10 @@ __device__ uint64_t wave_select_kth(const uint64_t* buf, int* hist, int cnt, int
 }
 
 // Keep exactly the W largest keys of buf[0..cnt) in buf[0..W).  Returns the
-// W-th key (the new threshold); cnt becomes W.
-__device__ uint64_t wave_compact(uint64_t* buf, uint64_t* surv, int* hist, int& cnt, int W, int lane, int* err) {
+// W-th key (the new threshold); cnt becomes W.  In place: a kept key moves
+// to pos + (kept lanes below it) <= its own index, and each group of 64 is
+// read before any of its writes, so no key is overwritten before it is read.
+__device__ uint64_t wave_compact(uint64_t* buf, int* hist, int& cnt, int W, int lane, int* err) {
     const uint64_t kth = wave_select_kth(buf, hist, cnt, W, lane, err);
     int pos = 0;
     for (int i0 = 0; i0 < cnt; i0 += kWLanes) {
@@ -416,11 +422,9 @@ __device__ uint64_t wave_compact(uint64_t* buf, uint64_t* surv, int* hist, int& 
         const uint64_t key = i < cnt ? buf[i] : 0ull;
         const bool keep = i < cnt && key >= kth;
         const uint64_t m = __ballot(keep);
-        if (keep && pos + lanes_below(m) < W) surv[pos + lanes_below(m)] = key;   // exactly W for distinct keys
+        if (keep && pos + lanes_below(m) < W) buf[pos + lanes_below(m)] = key;   // exactly W for distinct keys
         pos += __popcll(m);
     }
-    wave_fence();
-    for (int i = lane; i < W; i += kWLanes) buf[i] = surv[i];
     wave_fence();
     cnt = W;
     return kth;
@@ -499,8 +503,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage1_kernel(const TopkParam
     const int64_t end = min(total, a + p.seg);
     uint64_t* buf = wave_lds + (size_t)wave * wave_lds_words(W);
     const int soft = wave_soft_cap(W);
-    uint64_t* surv = buf + soft + kWRound;
-    int* hist = (int*)(surv + ((W + 1) & ~1));
+    int* hist = (int*)(buf + soft + kWRound);
 
     int r = (int)(a / req_len);
     const int m_slots = topk_slots(W);
@@ -523,7 +526,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage1_kernel(const TopkParam
     // and the q-th of them.
     auto shrink = [&]() {
         wave_fence();
-        const uint64_t own = wave_compact(buf, surv, hist, cnt, W, lane, p.err);
+        const uint64_t own = wave_compact(buf, hist, cnt, W, lane, p.err);
         thr = own > thr ? own : thr;
         const uint64_t oq = q < W ? wave_select_kth(buf, hist, W, q, lane, p.err) : own;
         wave_fence();
@@ -740,8 +743,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_logits_stage1_kernel(const To
     const int64_t end = min(total, a + p.seg);
     uint64_t* buf = wave_lds + (size_t)wave * wave_lds_words(W);
     const int soft = wave_soft_cap(W);
-    uint64_t* surv = buf + soft + kWRound;
-    int* hist = (int*)(surv + ((W + 1) & ~1));
+    int* hist = (int*)(buf + soft + kWRound);
 
     constexpr int NV = BF16 ? 1 : kWPerLane / 4;               // 16-byte registers per round
     // element k (0..7) of this lane in round rd
@@ -762,7 +764,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_logits_stage1_kernel(const To
         float lm = kLogitFloor, ls = 0.f;                       // lane's running max, sum of exp(x - lm)
         auto shrink = [&]() {
             wave_fence();
-            const uint64_t own = wave_compact(buf, surv, hist, cnt, W, lane, p.err);
+            const uint64_t own = wave_compact(buf, hist, cnt, W, lane, p.err);
             thr = own > thr ? own : thr;
             wave_fence();
         };
