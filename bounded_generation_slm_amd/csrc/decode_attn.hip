@@ -20,6 +20,9 @@
 // current beam order (parent's history rows + the new row), so the reorder
 // after the previous merge costs no separate pass.
 #include <mutex>
+#include <type_traits>
+
+#include "attn_tile.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(NTHR, (D == 64 ? 4 : 2)) void beam_decode_attn_kern
     }
     __syncthreads();
 
-    const int nkc = PP / 64;                      // 64-key prompt chunks
+    const float c = p.scale_log2;
     for (int blk = row0 + wave * 32; blk < row1; blk += 32 * (NTHR / kWave)) {
         const int m = blk + n;                    // this lane's query row
         const bool valid = m < row1;
@@ -166,8 +169,13 @@ __global__ __launch_bounds__(NTHR, (D == 64 ? 4 : 2)) void beam_decode_attn_kern
             for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
         float mrun = -INFINITY, lsum = 0.f;
 
-        for (int kc = 0; kc < nkc; ++kc) {
-            const int k0 = kc * 64;
+        // ---- prompt keys, 64 at a time ----
+        // Running max in raw score units with the scale folded into exp2; the
+        // reference max may trail the true one by up to kMaxLag (log2 units),
+        // so O and the row sum are rescaled only when some row's max moves
+        // further (after the first chunk almost never).  Only the last chunk
+        // of a prompt whose length is not a multiple of 64 masks keys >= P.
+        auto chunk = [&](int k0, auto masked) {
             f32x16 sacc[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -180,37 +188,42 @@ __global__ __launch_bounds__(NTHR, (D == 64 ? 4 : 2)) void beam_decode_attn_kern
                                                                        sacc[kb], 0, 0, 0);
                 }
             }
-            const bool tail = k0 + 64 > P;
+            if constexpr (decltype(masked)::value) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (k0 + kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3) >= P) sacc[kb][i] = -INFINITY;
+            }
             float tmax = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float x = sacc[kb][i] * p.scale_log2;
-                    if (tail && k0 + kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3) >= P) x = -INFINITY;
-                    sacc[kb][i] = x;
-                    tmax = fmaxf(tmax, x);
-                }
+                for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[kb][i]);
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
             const float mnew = fmaxf(mrun, tmax);  // finite: every chunk holds a prompt key
-            const float alpha = fast_exp2(mrun - mnew);
-            mrun = mnew;
+            if (__ballot((mnew - mrun) * c > kMaxLag) != 0) {   // mrun = -inf on the first chunk: taken
+                const float alpha = fast_exp2((mrun - mnew) * c);
+                lsum *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+                mrun = mnew;
+            }
+            const float mc = mrun * c;
             float psum = 0.f;
             uint32_t pk[2][8];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; i += 2) {
-                    const float p0 = fast_exp2(sacc[kb][i] - mnew);
-                    const float p1 = fast_exp2(sacc[kb][i + 1] - mnew);
+                    const float p0 = fast_exp2(fmaf(sacc[kb][i], c, -mc));
+                    const float p1 = fast_exp2(fmaf(sacc[kb][i + 1], c, -mc));
                     psum += p0 + p1;
                     pk[kb][i >> 1] = pack_bf16x2(p0, p1);
                 }
-            lsum = lsum * alpha + psum;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+            lsum += psum;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -222,7 +235,11 @@ __global__ __launch_bounds__(NTHR, (D == 64 ? 4 : 2)) void beam_decode_attn_kern
                         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pb), o[db], 0, 0, 0);
                     }
                 }
-        }
+        };
+        const int nfull = P / 64;
+        for (int kc = 0; kc < nfull; ++kc) chunk(kc * 64, std::false_type{});
+        if (P % 64 != 0) chunk(nfull * 64, std::true_type{});
+        mrun *= c;                                // scaled (log2) units from here on
 
         // ---- the beam's own suffix: parent's history rows, then the new row ----
         if (src < 0 || src >= W) src = w;         // flagged by the suffix copy above
