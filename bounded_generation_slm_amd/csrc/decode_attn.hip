@@ -389,26 +389,45 @@ __global__ __launch_bounds__(NTHR, (D == 64 ? 4 : 2)) void beam_decode_attn_kern
     }
 }
 
+// Rows of a (layer, request, KV head) unit are split over `chunks`
+// workgroups of whole 32-row blocks.  Cost model: the launch runs in
+// ceil(workgroups / resident) rounds, and a round lasts as long as its
+// busiest wave's blocks plus the prompt staging (taken as half a block);
+// the split with the least cost wins, the fewest chunks on ties.
+int decode_chunks(int64_t units, int blocks32, int waves, int64_t resident) {
+    int best = 1;
+    int64_t best_cost = INT64_MAX;
+    for (int c = 1; c <= blocks32; ++c) {
+        const int per_wg = (blocks32 + c - 1) / c;
+        const int per_wave = (per_wg + waves - 1) / waves;
+        const int64_t rounds = (units * c + resident - 1) / resident;
+        const int64_t cost = rounds * (2 * per_wave + 1);
+        if (cost < best_cost) {
+            best = c;
+            best_cost = cost;
+        }
+        if (per_wave == 1) break;                 // more chunks only add staging
+    }
+    return best;
+}
+
 template <int D, bool OUT_BF16, int NTHR, bool STAGE>
-hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_variant(const DecodeParams& p, int num_cus, hipStream_t stream) {
     const int n_units = p.n_layers * p.num_requests * p.n_heads_kv;
     const int M = p.width * p.group;
     const int blocks32 = (M + 31) / 32;
-    // enough workgroups to fill 256 CUs a few times over, whole 32-row blocks each
-    int chunks = (1024 + n_units - 1) / n_units;
-    chunks = max(1, min(chunks, blocks32));
-    const int chunk_rows = (blocks32 + chunks - 1) / chunks * 32;
-    chunks = (M + chunk_rows - 1) / chunk_rows;
     const int64_t units_padded = ((int64_t)n_units + kNumXcd - 1) / kNumXcd * kNumXcd;
-    const int64_t blocks = units_padded * chunks;
-    if (blocks == 0) return hipSuccess;
+    if (units_padded == 0 || blocks32 == 0) return hipSuccess;
     const size_t lds = DecodeLds<D>::bytes(p.prompt_len) + (STAGE ? (NTHR / kWave) * kStageWaveBytes : 0);
     auto kern = beam_decode_attn_kernel<D, OUT_BF16, NTHR, STAGE>;
     // raise the kernel's dynamic-LDS limit only when a call needs more than
-    // before (no host call per launch, so launches can be graph-captured);
-    // the lock keeps the recorded limit and the attribute in step across threads
+    // before (no host call per launch, so launches can be graph-captured), and
+    // query the workgroups per CU once per LDS size; the lock keeps the
+    // recorded values and the attribute in step across threads
     static std::mutex lds_mu;
-    static size_t lds_limit = 0;
+    static size_t lds_limit = 0, occ_lds = 0;
+    static int occ = 1;
+    int per_cu;
     {
         std::lock_guard<std::mutex> lock(lds_mu);
         if (lds > lds_limit) {
@@ -416,7 +435,19 @@ hipError_t launch_variant(const DecodeParams& p, hipStream_t stream) {
             if (e != hipSuccess) return e;
             lds_limit = lds;
         }
+        if (lds != occ_lds) {
+            int n = 0;
+            hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)kern, NTHR, lds);
+            if (e != hipSuccess) return e;
+            occ = max(1, n);
+            occ_lds = lds;
+        }
+        per_cu = occ;
     }
+    int chunks = decode_chunks(units_padded, blocks32, NTHR / kWave, (int64_t)num_cus * per_cu);
+    const int chunk_rows = (blocks32 + chunks - 1) / chunks * 32;
+    chunks = (M + chunk_rows - 1) / chunk_rows;
+    const int64_t blocks = units_padded * chunks;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NTHR), lds, stream, p, chunks, chunk_rows);
     return hipGetLastError();
 }
@@ -427,7 +458,7 @@ size_t beam_decode_lds_bytes(int head_dim, int prompt_len) {
     return head_dim == 128 ? DecodeLds<128>::bytes(prompt_len) : DecodeLds<64>::bytes(prompt_len);
 }
 
-hipError_t launch_beam_decode_attn(const DecodeParams& p, int head_dim, bool out_bf16,
+hipError_t launch_beam_decode_attn(const DecodeParams& p, int head_dim, bool out_bf16, int num_cus,
                                    hipStream_t stream) {
     // A prompt copy too large for two workgroups per CU is shared by 16 waves
     // (head_dim 64; at 128 the registers of 16 waves would not hold a lane's state).
@@ -437,12 +468,14 @@ hipError_t launch_beam_decode_attn(const DecodeParams& p, int head_dim, bool out
     const bool wide = head_dim == 64 && prompt_lds > kDecSmallLds;
     const bool stage = head_dim == 64 && !out_bf16 && prompt_lds + 8 * kStageWaveBytes <= kDecSmallLds;
     if (head_dim == 128)
-        return out_bf16 ? launch_variant<128, true, 512, false>(p, stream)
-                        : launch_variant<128, false, 512, false>(p, stream);
+        return out_bf16 ? launch_variant<128, true, 512, false>(p, num_cus, stream)
+                        : launch_variant<128, false, 512, false>(p, num_cus, stream);
     if (out_bf16)
-        return wide ? launch_variant<64, true, 1024, false>(p, stream) : launch_variant<64, true, 512, false>(p, stream);
-    if (stage) return launch_variant<64, false, 512, true>(p, stream);
-    return wide ? launch_variant<64, false, 1024, false>(p, stream) : launch_variant<64, false, 512, false>(p, stream);
+        return wide ? launch_variant<64, true, 1024, false>(p, num_cus, stream)
+                    : launch_variant<64, true, 512, false>(p, num_cus, stream);
+    if (stage) return launch_variant<64, false, 512, true>(p, num_cus, stream);
+    return wide ? launch_variant<64, false, 1024, false>(p, num_cus, stream)
+                : launch_variant<64, false, 512, false>(p, num_cus, stream);
 }
 
 }  // namespace slm

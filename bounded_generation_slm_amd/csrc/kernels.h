@@ -105,7 +105,7 @@ struct DecodeParams {
     int n_heads_q, n_heads_kv, group;
     float scale_log2;
 };
-hipError_t launch_beam_decode_attn(const DecodeParams& p, int head_dim, bool out_bf16,
+hipError_t launch_beam_decode_attn(const DecodeParams& p, int head_dim, bool out_bf16, int num_cus,
                                    hipStream_t stream);
 
 struct TopkParams {

@@ -388,7 +388,8 @@ slm_status slm_beam_decode_attn(slm_ctx* ctx, const slm_beam_attn_args* a) {
     p.hist_len = a->hist_len; p.suffix_cap = a->suffix_cap; p.n_heads_q = a->n_heads_q;
     p.n_heads_kv = a->n_heads_kv; p.group = a->n_heads_q / a->n_heads_kv;
     p.scale_log2 = a->scale * 1.4426950408889634f;
-    return SLM_LAUNCH(ctx, slm::launch_beam_decode_attn(p, a->head_dim, a->out_dtype == SLM_BF16, ctx->stream),
+    return SLM_LAUNCH(ctx, slm::launch_beam_decode_attn(p, a->head_dim, a->out_dtype == SLM_BF16, ctx->num_cus,
+                                                                ctx->stream),
                       "decode");
 }
 
