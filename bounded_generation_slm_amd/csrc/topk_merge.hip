@@ -29,6 +29,7 @@
 // one compare.  Insertion compacts each wave's survivors with ballots.
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -296,7 +297,12 @@ __device__ __forceinline__ uint64_t* req_slot(const TopkParams& p, int r, int s)
 constexpr int kWLanes = 64;
 constexpr int kWPerLane = 8;                        // candidates per lane per round
 constexpr int kWRound = kWLanes * kWPerLane;        // 512
-constexpr int kWDepth = 4;                          // rounds in flight
+// Rounds in flight per wave: 4 where four workgroups share a CU (W <= 256),
+// 8 where the wider buffers leave room for three (their registers allow it,
+// and fewer waves each need more bytes in flight).
+__host__ __device__ constexpr int stream_depth(bool wide) { return wide ? 8 : 4; }
+__host__ __device__ inline bool wide_width(int W) { return W > kWRound / 2; }
+constexpr int kWDepth = 4;                          // the merge on logits: rounds in flight
 constexpr int kWBins = 256;
 
 // LDS layout of one wave, in 8-byte words: buf[soft + kWRound], hist[kWBins]
@@ -305,7 +311,7 @@ constexpr int kWBins = 256;
 // keeps a round's worth of slots (512) free after a compaction; narrower
 // ones compact at 512 keys, which raises their threshold sooner.  Four
 // workgroups fit a CU up to W = 256, three up to W = 512.
-__host__ __device__ inline int wave_soft_cap(int W) { return W > kWRound / 2 ? W + kWRound : kWRound; }
+__host__ __device__ inline int wave_soft_cap(int W) { return wide_width(W) ? W + kWRound : kWRound; }
 __host__ __device__ inline int wave_lds_words(int W) {
     return wave_soft_cap(W) + kWRound + kWBins / 2;
 }
@@ -484,13 +490,25 @@ __device__ __forceinline__ uint64_t round_bound(const float (&sc)[kWPerLane], co
 // non-temporal policy (measured faster than cached loads on this path).  All
 // loads are ordinary compiler-visible loads, so the compiler tracks their
 // destination registers and places the waits.
+// f(integral_constant<int, 0>), f(..1), ... f(..N-1) in order while each
+// returns true; true if all did.
+template <class F, int... J>
+__device__ __forceinline__ bool for_each_step_impl(F&& f, std::integer_sequence<int, J...>) {
+    return (f(std::integral_constant<int, J>{}) && ...);
+}
+template <int N, class F>
+__device__ __forceinline__ bool for_each_step(F&& f) {
+    return for_each_step_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 __device__ __forceinline__ f32x4 stream_load16(const float* p) {
     return __builtin_nontemporal_load((const f32x4*)p);
 }
 __device__ __forceinline__ float stream_load4(const float* p) { return __builtin_nontemporal_load(p); }
 
-template <bool VEC>
-__global__ __launch_bounds__(kTkThreads) void topk_stage1_kernel(const TopkParams p) {
+template <bool VEC, int DEPTH>
+__global__ __launch_bounds__(kTkThreads, (DEPTH == stream_depth(false) ? 4 : 3)) void topk_stage1_kernel(
+    const TopkParams p) {
     extern __shared__ __attribute__((aligned(16))) uint64_t wave_lds[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -584,10 +602,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage1_kernel(const TopkParam
         const uint32_t f0 = (uint32_t)(a - (int64_t)r * req_len);   // flat index b*V + v of lp[0]
         const uint64_t* baddr = bound_addr(p, r, lane, m_slots);
         const int rounds = (n + kWRound - 1) / kWRound;
-        f32x4 B0[NV], B1[NV], B2[NV], B3[NV];
+        f32x4 B[DEPTH][NV];
         // loads of round rd (clamped into the piece: rounds past its end
         // re-read valid addresses, and their values are never used)
-        auto fetch = [&](int rd, f32x4 (&dst)[NV]) {
+        auto fetch = [&](int rd, f32x4 (&dst)[NV]) __attribute__((always_inline)) {
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
                 const int i0 = rd * kWRound + (j * kWLanes + lane) * 4;
@@ -599,7 +617,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage1_kernel(const TopkParam
                 }
             }
         };
-        auto round = [&](int rd, f32x4 (&src)[NV]) {
+        auto round = [&](int rd, f32x4 (&src)[NV]) __attribute__((always_inline)) {
             float sc[kWPerLane];
 #pragma unroll
             for (int j = 0; j < NV; ++j)
@@ -636,29 +654,35 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage1_kernel(const TopkParam
                 }
             if (cnt > soft) shrink();
         };
-        // Four rounds of loads stay in flight; the shared bound is read once
-        // per group of four rounds, issued with the group's first loads and
-        // taken up at its last round.
-        fetch(0, B0);
-        fetch(1, B1);
-        fetch(2, B2);
+        // DEPTH rounds of loads stay in flight: before round rd + j the loads
+        // of round rd + j + DEPTH - 1 go out into the buffer round rd + j - 1
+        // freed.  The shared bound is read once per group of DEPTH rounds,
+        // issued with the group's first loads and taken up at its last round.
+        // (Each step is its own instantiation, so every buffer index is a
+        // constant and the buffers stay in registers.)
         uint64_t sh = 0;
-        for (int rd = 0; rd < rounds; rd += kWDepth) {
-            fetch(rd + 3, B3);
-            sh = load_relaxed(baddr);
-            round(rd, B0);
-            if (rd + 1 >= rounds) break;
-            fetch(rd + 4, B0);
-            round(rd + 1, B1);
-            if (rd + 2 >= rounds) break;
-            fetch(rd + 5, B1);
-            round(rd + 2, B2);
-            if (rd + 3 >= rounds) break;
-            fetch(rd + 6, B2);
-            const uint64_t u = bound_take(sh, lane, m_slots);
-            thr = u > thr ? u : thr;
-            round(rd + 3, B3);
-        }
+        int rd = 0;
+        auto step = [&](auto jc) __attribute__((always_inline)) {   // false once the piece is done
+            constexpr int j = decltype(jc)::value;
+            if constexpr (j == 0) {
+                fetch(rd + DEPTH - 1, B[DEPTH - 1]);
+                sh = load_relaxed(baddr);
+            } else {
+                fetch(rd + DEPTH - 1 + j, B[j - 1]);
+            }
+            if constexpr (j == DEPTH - 1) {
+                const uint64_t u = bound_take(sh, lane, m_slots);
+                thr = u > thr ? u : thr;
+            }
+            round(rd + j, B[j]);
+            return rd + j + 1 < rounds;                         // wave-uniform
+        };
+        for_each_step<DEPTH - 1>([&](auto jc) __attribute__((always_inline)) {
+            fetch(decltype(jc)::value, B[decltype(jc)::value]);
+            return true;
+        });
+        for (; rd < rounds; rd += DEPTH)
+            if (!for_each_step<DEPTH>(step)) break;
         a = pe;
     }
     flush();
@@ -1073,10 +1097,11 @@ hipError_t launch_beam_topk_merge(const TopkParams& p, hipStream_t stream) {
     const int64_t blocks = (waves + kTkThreads / kWLanes - 1) / (kTkThreads / kWLanes);
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const size_t lds = beam_topk_stage1_lds(p.width);
-    if (vec)
-        hipLaunchKernelGGL(topk_stage1_kernel<true>, dim3((unsigned)blocks), dim3(kTkThreads), lds, stream, p);
-    else
-        hipLaunchKernelGGL(topk_stage1_kernel<false>, dim3((unsigned)blocks), dim3(kTkThreads), lds, stream, p);
+    constexpr int D4 = stream_depth(false), D8 = stream_depth(true);
+    const bool wide = wide_width(p.width);
+    auto kern = vec ? (wide ? topk_stage1_kernel<true, D8> : topk_stage1_kernel<true, D4>)
+                    : (wide ? topk_stage1_kernel<false, D8> : topk_stage1_kernel<false, D4>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kTkThreads), lds, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_stage2_kernel, dim3(p.num_requests), dim3(kTkThreads), 0, stream, p);
@@ -1172,7 +1197,9 @@ int beam_topk_logits_blocks_per_cu(int width) {
 int beam_topk_blocks_per_cu(int width) {
     int n = 0;
     const size_t lds = beam_topk_stage1_lds(width);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)topk_stage1_kernel<true>, kTkThreads, lds) !=
+    const void* kern = wide_width(width) ? (const void*)topk_stage1_kernel<true, stream_depth(true)>
+                                         : (const void*)topk_stage1_kernel<true, stream_depth(false)>;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kTkThreads, lds) !=
             hipSuccess || n <= 0)
         n = 1;
     return n;
