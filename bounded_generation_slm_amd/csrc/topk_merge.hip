@@ -237,26 +237,24 @@ __device__ __forceinline__ void insert(SelectorLds& s, const uint64_t (&keys)[kP
         if (keys[e] > thr) s.buf[base + off[e]] = keys[e];
 }
 
-// Bitonic sort of s.buf[0..S) descending, S a power of two <= 512 (entries
-// >= n padded with 0, which ranks below every key).
-__device__ void sort_desc(SelectorLds& s, int n, int S) {
-    for (int i = threadIdx.x + n; i < S; i += kTkThreads) s.buf[i] = 0;
-    __syncthreads();
-    for (int size = 2; size <= S; size <<= 1)
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const int t = threadIdx.x;              // one pair per thread, S / 2 <= 256 pairs
-            if (t < S / 2) {
-                const int i = 2 * t - (t & (stride - 1));
-                const int j = i + stride;
-                const bool desc = (i & size) == 0;
-                const uint64_t a = s.buf[i], b = s.buf[j];
-                if ((a < b) == desc) {
-                    s.buf[i] = b;
-                    s.buf[j] = a;
-                }
-            }
-            __syncthreads();
+// The W kept keys s.buf[0..n) in descending order, with no sort: keys are
+// distinct, so a key's position is the number of kept keys above it (one
+// pass of LDS broadcast reads per key, no barrier).  out(pos, key) for every
+// pos < W; positions n..W-1 (fewer than W keys) get key 0, which ranks below
+// every key.  s.buf must be final (after a barrier).
+template <class F>
+__device__ __forceinline__ void write_ranked(const SelectorLds& s, int n, int W, F&& out) {
+    for (int j = threadIdx.x; j < W; j += kTkThreads) {
+        if (j >= n) {
+            out(j, 0ull);
+            continue;
         }
+        const uint64_t key = s.buf[j];
+        int pos = 0;
+#pragma unroll 8
+        for (int i = 0; i < n; ++i) pos += s.buf[i] > key ? 1 : 0;
+        out(pos, key);
+    }
 }
 
 __device__ __forceinline__ uint64_t load_relaxed(const uint64_t* p) {
@@ -714,16 +712,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage2_kernel(const TopkParam
         if (s.cnt > kSoftCap) compact(s, W, p.err);
     }
     compact(s, W, p.err);
-    int S = 2;
-    while (S < W) S <<= 1;
-    sort_desc(s, min(s.cnt, W), S);
-    for (int j = threadIdx.x; j < W; j += kTkThreads) {
-        const uint64_t key = s.buf[j];
+    write_ranked(s, min(s.cnt, W), W, [&](int j, uint64_t key) {
         const uint32_t f = 0xFFFFFFFFu - (uint32_t)key;
         p.tokens[(int64_t)r * W + j] = (int32_t)(f % (uint32_t)V);
         p.parent[(int64_t)r * W + j] = (int32_t)(f / (uint32_t)V);
         p.cum_out[(int64_t)r * W + j] = unorder_f32((uint32_t)(key >> 32));
-    }
+    });
     // leave the request's shared state cleared for the next call
     if (threadIdx.x < kSlot0 + kMaxSlots)       // words 0..63: threshold, count, slots
         __hip_atomic_store(p.req_state + (int64_t)r * kTopkStateWords + threadIdx.x, 0ull, __ATOMIC_RELAXED,
@@ -1033,16 +1027,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_logits_final_kernel(const Top
         if (s.cnt > kSoftCap) compact(s, W, p.err);
     }
     compact(s, W, p.err);
-    int S2 = 2;
-    while (S2 < W) S2 <<= 1;
-    sort_desc(s, min(s.cnt, W), S2);
-    for (int j = threadIdx.x; j < W; j += kTkThreads) {
-        const uint64_t key = s.buf[j];
+    write_ranked(s, min(s.cnt, W), W, [&](int j, uint64_t key) {
         const uint32_t f = 0xFFFFFFFFu - (uint32_t)key;
         p.tokens[(int64_t)r * W + j] = (int32_t)(f % (uint32_t)V);
         p.parent[(int64_t)r * W + j] = (int32_t)(f / (uint32_t)V);
         p.cum_out[(int64_t)r * W + j] = unorder_f32((uint32_t)(key >> 32));
-    }
+    });
     if (threadIdx.x < kSlot0 + kMaxSlots)       // leave the request's state line cleared
         __hip_atomic_store(p.req_state + (int64_t)r * kTopkStateWords + threadIdx.x, 0ull, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);

@@ -119,11 +119,23 @@ def test_decode_tiny_workload(gpu, hist, out_dtype):
     (1, 3, 9, 65, 4, 3, 6, 3, 64, True),      # a 1-key tail chunk
     (1, 2, 7, 200, 8, 7, 8, 2, 128, True),    # head_dim 128, longest suffix
     (3, 2, 33, 130, 5, 4, 14, 2, 64, False),  # identity parent
+    (1, 1, 100, 70, 3, 2, 14, 2, 64, True),   # one unit: its 700 rows split over 3 workgroups
 ])
 def test_decode_shapes(gpu, NL, R, W, P, S_cap, hist, Hq, Hkv, D, parent):
     note("decode NL=%d R=%d W=%d P=%d hist=%d Hq=%d Hkv=%d D=%d" % (NL, R, W, P, hist, Hq, Hkv, D))
     c = _decode_case(P * 7 + W, NL, R, W, P, S_cap, hist, Hq, Hkv, D, parent)
     _decode_check(gpu, c, "decode shape")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("NL,R,W,P,hist", [(1, 2, 5, 300, 2), (2, 1, 80, 333, 4)])
+def test_decode_long_prompt_forms(gpu, NL, R, W, P, hist, out_dtype):
+    """Prompts whose LDS copy leaves room for one workgroup per CU (the
+    16-wave form, unstaged output) with a ragged last 64-key chunk; few units
+    and many rows, so the rows of a unit are split over several workgroups."""
+    note("decode long-prompt form NL=%d R=%d W=%d P=%d hist=%d out=%s" % (NL, R, W, P, hist, out_dtype))
+    c = _decode_case(P + W * 3 + hist, NL, R, W, P, hist + 1, hist, 14, 2, 64, True)
+    _decode_check(gpu, c, "decode long-prompt form", out_dtype)
 
 
 @pytest.mark.parametrize("shape", [wl.BEAM_SHORT, wl.BEAM_LONG], ids=lambda s: s.name)
