@@ -86,11 +86,22 @@ __global__ __launch_bounds__(NTHR, (D == 64 ? 4 : 2)) void beam_decode_attn_kern
     {
         const uint16_t* pk = p.prefix_k + (int64_t)lr * P * kv_row + (int64_t)g * D;
         const uint16_t* pv = p.prefix_v + (int64_t)lr * P * kv_row + (int64_t)g * D;
+        // K rows in batches of KU chunks per thread: a batch's loads all go out
+        // before its LDS writes, so a batch costs one memory round trip
+        constexpr int KU = 4;
         const int kchunks = PP * (D / 8);
-        for (int c = tid; c < kchunks; c += NTHR) {
-            const int key = c / (D / 8), dg = c % (D / 8);
-            const u32x4 x = key < P ? *(const u32x4*)(pk + key * kv_row + dg * 8) : u32x4{0u, 0u, 0u, 0u};
-            *(u32x4*)(k_lds + key * KROW + dg * 8) = x;
+        for (int c0 = tid; c0 < kchunks; c0 += NTHR * KU) {
+            u32x4 x[KU];
+#pragma unroll
+            for (int u = 0; u < KU; ++u) {
+                const int c = c0 + u * NTHR, key = c / (D / 8), dg = c % (D / 8);
+                x[u] = c < kchunks && key < P ? *(const u32x4*)(pk + key * kv_row + dg * 8) : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < KU; ++u) {
+                const int c = c0 + u * NTHR, key = c / (D / 8), dg = c % (D / 8);
+                if (c < kchunks) *(u32x4*)(k_lds + key * KROW + dg * 8) = x[u];
+            }
         }
         // V^T: unit = (16-key chunk c16, half vh, d-group dg); keys 16c16 + 8(e/4) + 4vh + e%4
         const int vunits = (PP / 16) * 2 * (D / 8);
@@ -122,25 +133,52 @@ __global__ __launch_bounds__(NTHR, (D == 64 ? 4 : 2)) void beam_decode_attn_kern
         const int rows_out = p.hist_len + 1;
         const int cpr = D / 8;                                          // 16-byte chunks per row
         const int total = (wb1 - wb0) * rows_out * cpr;
-        for (int c = tid; c < total; c += NTHR) {
-            const int part = c % cpr;
-            const int i = (c / cpr) % rows_out;
-            const int w = wb0 + c / (cpr * rows_out);
-            const int64_t dst = ((((int64_t)lr * W + w) * p.suffix_cap + i) * Hkv + g) * D + part * 8;
-            const uint16_t *ks, *vs;
-            if (i < p.hist_len) {
-                int src = p.parent ? p.parent[r * W + w] : w;
-                if (src < 0 || src >= W) { raise_error(p.err, kErrParent); src = w; }
-                const int64_t so = ((((int64_t)lr * W + src) * p.suffix_cap + i) * Hkv + g) * D + part * 8;
-                ks = p.suffix_k_in + so;
-                vs = p.suffix_v_in + so;
-            } else {
-                const int64_t so = (((int64_t)lr * W + w) * Hkv + g) * D + part * 8;
-                ks = p.k_new + so;
-                vs = p.v_new + so;
+        // in batches of CU chunks per thread: parent indices, then the rows,
+        // then the stores (two memory round trips per batch)
+        constexpr int CU = 4;
+        for (int c0 = tid; c0 < total; c0 += NTHR * CU) {
+            int src[CU];
+#pragma unroll
+            for (int u = 0; u < CU; ++u) {
+                const int c = c0 + u * NTHR;
+                const int i = (c / cpr) % rows_out, w = wb0 + c / (cpr * rows_out);
+                src[u] = c < total && i < p.hist_len && p.parent ? p.parent[r * W + w] : w;
             }
-            *(u32x4*)(p.suffix_k_out + dst) = *(const u32x4*)ks;
-            *(u32x4*)(p.suffix_v_out + dst) = *(const u32x4*)vs;
+            u32x4 kx[CU], vx[CU];
+#pragma unroll
+            for (int u = 0; u < CU; ++u) {
+                const int c = c0 + u * NTHR;
+                const int part = c % cpr, i = (c / cpr) % rows_out, w = wb0 + c / (cpr * rows_out);
+                kx[u] = vx[u] = u32x4{0u, 0u, 0u, 0u};
+                if (c < total) {
+                    const uint16_t *ks, *vs;
+                    if (i < p.hist_len) {
+                        if (src[u] < 0 || src[u] >= W) {
+                            raise_error(p.err, kErrParent);
+                            src[u] = w;
+                        }
+                        const int64_t so = ((((int64_t)lr * W + src[u]) * p.suffix_cap + i) * Hkv + g) * D + part * 8;
+                        ks = p.suffix_k_in + so;
+                        vs = p.suffix_v_in + so;
+                    } else {
+                        const int64_t so = (((int64_t)lr * W + w) * Hkv + g) * D + part * 8;
+                        ks = p.k_new + so;
+                        vs = p.v_new + so;
+                    }
+                    kx[u] = *(const u32x4*)ks;
+                    vx[u] = *(const u32x4*)vs;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < CU; ++u) {
+                const int c = c0 + u * NTHR;
+                const int part = c % cpr, i = (c / cpr) % rows_out, w = wb0 + c / (cpr * rows_out);
+                if (c < total) {
+                    const int64_t dst = ((((int64_t)lr * W + w) * p.suffix_cap + i) * Hkv + g) * D + part * 8;
+                    *(u32x4*)(p.suffix_k_out + dst) = kx[u];
+                    *(u32x4*)(p.suffix_v_out + dst) = vx[u];
+                }
+            }
         }
     }
     __syncthreads();
