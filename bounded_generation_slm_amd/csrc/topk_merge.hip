@@ -582,7 +582,6 @@ __global__ __launch_bounds__(kTkThreads, (DEPTH == stream_depth(false) ? 4 : 3))
     };
 
     constexpr int NV = kWPerLane / 4;
-    constexpr int LPF = VEC ? NV : kWPerLane;                   // load instructions per round
     while (a < end) {
         const int64_t row = a / V;                              // r * Win + b
         const int rr = (int)(row / p.beams_in);
