@@ -4,7 +4,8 @@ load that is still in flight.
 
 LDS loads (and other LGKM-counted operations) complete in issue order and are
 covered by `s_waitcnt lgkmcnt(N)`; vector-memory loads and stores likewise by
-`s_waitcnt vmcnt(N)`.  Loads issued through inline assembly are invisible to
+`s_waitcnt vmcnt(N)`.  Two loads of one counter may target the same register
+(the later one lands last); across the two counters they may not.  Loads issued through inline assembly are invisible to
 the compiler's own wait insertion, so this is the check that their waits are
 where the code assumes.  Tracking is per basic block (any branch or label
 resets it), so a load whose wait sits in another block is not followed."""
@@ -77,13 +78,13 @@ def hazards(asm_text):
                 owned |= d
             if touched & owned:
                 found.append((kern, no, s, name))
-        if is_load:                      # a new load also may not target a register still owned
-            for name, inflight in (("lgkmcnt", lgkm), ("vmcnt", vm)):
-                owned = set()
-                for d in inflight:
-                    owned |= d
-                if dest & owned:
-                    found.append((kern, no, s, name))
+        if is_load:                      # a new load may not target a register a load of the
+            other = vm if op.startswith("ds_") else lgkm    # other counter still owns (loads of one
+            owned = set()                                    # counter return in issue order)
+            for d in other:
+                owned |= d
+            if dest & owned:
+                found.append((kern, no, s, "vmcnt" if other is vm else "lgkmcnt"))
         if _is_lgkm(op):
             lgkm.append(dest if op.startswith(("ds_read", "ds_bpermute", "ds_permute")) else set())
         elif _is_vmem(op):
