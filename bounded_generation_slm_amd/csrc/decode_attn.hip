@@ -19,6 +19,7 @@
 // keys with vector dot products.  The workgroup also writes the suffix in the
 // current beam order (parent's history rows + the new row), so the reorder
 // after the previous merge costs no separate pass.
+#include <map>
 #include <mutex>
 #include <type_traits>
 
@@ -459,12 +460,12 @@ hipError_t launch_variant(const DecodeParams& p, int num_cus, hipStream_t stream
     const size_t lds = DecodeLds<D>::bytes(p.prompt_len) + (STAGE ? (NTHR / kWave) * kStageWaveBytes : 0);
     auto kern = beam_decode_attn_kernel<D, OUT_BF16, NTHR, STAGE>;
     // raise the kernel's dynamic-LDS limit only when a call needs more than
-    // before (no host call per launch, so launches can be graph-captured), and
-    // query the workgroups per CU once per LDS size; the lock keeps the
+    // before, and query the workgroups per CU once per LDS size (no host call
+    // per launch, so launches can be graph-captured); the lock keeps the
     // recorded values and the attribute in step across threads
     static std::mutex lds_mu;
-    static size_t lds_limit = 0, occ_lds = 0;
-    static int occ = 1;
+    static size_t lds_limit = 0;
+    static std::map<size_t, int> occ;            // workgroups per CU by LDS size
     int per_cu;
     {
         std::lock_guard<std::mutex> lock(lds_mu);
@@ -473,14 +474,14 @@ hipError_t launch_variant(const DecodeParams& p, int num_cus, hipStream_t stream
             if (e != hipSuccess) return e;
             lds_limit = lds;
         }
-        if (lds != occ_lds) {
+        auto it = occ.find(lds);
+        if (it == occ.end()) {
             int n = 0;
             hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)kern, NTHR, lds);
             if (e != hipSuccess) return e;
-            occ = max(1, n);
-            occ_lds = lds;
+            it = occ.emplace(lds, max(1, n)).first;
         }
-        per_cu = occ;
+        per_cu = it->second;
     }
     int chunks = decode_chunks(units_padded, blocks32, NTHR / kWave, (int64_t)num_cus * per_cu);
     const int chunk_rows = (blocks32 + chunks - 1) / chunks * 32;
