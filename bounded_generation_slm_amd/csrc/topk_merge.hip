@@ -14,14 +14,15 @@
 // A larger key ranks first, and no two keys are equal, so "the top W" is a
 // unique set and every selection below is exact.
 //
-// Two stages (both HBM-bound streaming, one pass over their input):
-//   stage 1: one workgroup per (request, beam row, vocabulary chunk) streams
-//            its log-probs, keeping the chunk's top W keys.  Exact: a global
-//            winner has fewer than W candidates of its own chunk above it.
-//            Short calls (the first merge has one row per request) split
-//            rows into chunks so that enough workgroups fill the GPU.
-//   stage 2: one workgroup per request streams the Win*W stage-1 keys, keeps
-//            the top W, sorts them and writes tokens, parents and scores.
+// Two stages:
+//   stage 1: the flattened candidates of the call are split into equal
+//            ranges, one per resident wave; a wave streams its range once,
+//            keeping its top W keys of each request against a threshold
+//            shared per request, and appends the keys not below that shared
+//            bound to the request's list.  Exact: every threshold is backed
+//            by W keys at or above it, so no final winner is dropped.
+//   stage 2: one workgroup per request reads its list, keeps the top W and
+//            writes tokens, parents and scores in rank order.
 // The streaming selector keeps candidates above a running threshold in an
 // LDS buffer; when the buffer passes a soft capacity it radix-selects the
 // W-th largest key (8-bit digits, wave64 scans), keeps the W keys at or above
@@ -283,7 +284,7 @@ __device__ __forceinline__ uint64_t* req_slot(const TopkParams& p, int r, int s)
     return p.req_state + (int64_t)r * kTopkStateWords + kSlot0 + s;
 }
 
-// ---- stage 1: one wave per (request, beam row, vocabulary chunk) ----
+// ---- stage 1: one wave per equal range of the flattened candidates ----
 //
 // Each wave owns a private LDS region (candidate buffer and 256 radix bins);
 // its candidate count and threshold live in wave-uniform registers, so the
