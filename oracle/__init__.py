@@ -50,7 +50,7 @@ def _load():
         lib.orc_prefill_attn.argtypes = [P, P, P, P, i32, i32, i32, i32, f64, P]
         lib.orc_prefill_attn_rows.argtypes = [P, P, P, P, i32, i32, i32, i32, f64, P, P, i64, P]
         lib.orc_gather_last.argtypes = [P, P, i32, i32, P]
-        lib.orc_beam_decode_attn.argtypes = [i32] * 9 + [f64] + [P] * 11
+        lib.orc_beam_decode_attn.argtypes = [i32] * 9 + [f64] + [P] * 12
         lib.orc_topk_merge.argtypes = [P, P, i32, i32, i32, i32, P, P, P]
         lib.orc_topk_merge_logits.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P]
         lib.orc_label_head.argtypes = [P, P, i32, i32, P, i32, P, i32, i32, P, P, P, P, P, P]
@@ -136,18 +136,27 @@ def label_head(hidden, cu_seqlens, lm_head, labels, k, label_map=None):
 
 
 def beam_decode_attn(q, prefix_k, prefix_v, suffix_k_in, suffix_v_in, k_new, v_new,
-                     parent, hist_len, scale=None):
+                     parent, hist_len, scale=None, prompt_cu=None):
     """Shared-prompt + per-beam-suffix decode attention.
 
-    q [NL,R,W,Hq,D]; prefix_k/v [NL,R,P,Hkv,D]; suffix_*_in [NL,R,W,S_cap,Hkv,D]
-    (rows < hist_len valid, previous beam order); k_new/v_new [NL,R,W,Hkv,D];
-    parent [R,W] int32 or None (identity).
+    q [NL,R,W,Hq,D]; prefix_k/v [NL,R,P,Hkv,D], or with prompt_cu (R+1
+    offsets) prompts of different lengths packed per layer as
+    [NL,prompt_cu[R],Hkv,D] (request r: rows prompt_cu[r]..prompt_cu[r+1]);
+    suffix_*_in [NL,R,W,S_cap,Hkv,D] (rows < hist_len valid, previous beam
+    order); k_new/v_new [NL,R,W,Hkv,D]; parent [R,W] int32 or None (identity).
     Returns (out [NL,R,W,Hq,D] float64, suffix_k_out, suffix_v_out), the
     suffix outputs holding rows 0..hist_len (zeros above)."""
     q = _c(q, np.uint16)
     NL, R, W, Hq, D = q.shape
     pk, pv = _c(prefix_k, np.uint16), _c(prefix_v, np.uint16)
-    P, Hkv = pk.shape[2], pk.shape[3]
+    cu = None
+    if prompt_cu is None:
+        P, Hkv = pk.shape[2], pk.shape[3]
+    else:
+        cu = _c(prompt_cu, np.int32)
+        if cu.shape != (R + 1,) or pk.shape[:2] != (NL, int(cu[-1])):
+            raise ValueError("beam_decode_attn: prompt_cu / packed prompt shape mismatch")
+        P, Hkv = int(np.max(np.diff(cu), initial=0)), pk.shape[2]
     sk, sv = _c(suffix_k_in, np.uint16), _c(suffix_v_in, np.uint16)
     S_cap = sk.shape[3]
     kn, vn = _c(k_new, np.uint16), _c(v_new, np.uint16)
@@ -158,7 +167,7 @@ def beam_decode_attn(q, prefix_k, prefix_v, suffix_k_in, suffix_v_in, k_new, v_n
     svo = np.zeros(sv.shape, np.uint16)
     _check(_load().orc_beam_decode_attn(NL, R, W, P, int(hist_len), S_cap, Hq, Hkv, D, scale,
                                         _p(q), _p(pk), _p(pv), _p(sk), _p(sv), _p(kn), _p(vn),
-                                        _p(par), _p(out), _p(sko), _p(svo)), "beam_decode_attn")
+                                        _p(par), _p(cu), _p(out), _p(sko), _p(svo)), "beam_decode_attn")
     return out, sko, svo
 
 

@@ -219,11 +219,21 @@ int orc_beam_decode_attn(int NL, int R, int W, int P, int hist, int S_cap,
                          const uint16_t *prefix_v, const uint16_t *sk_in,
                          const uint16_t *sv_in, const uint16_t *k_new,
                          const uint16_t *v_new, const int32_t *parent,
+                         const int32_t *prompt_cu,
                          double *out, uint16_t *sk_out, uint16_t *sv_out)
 {
     if (NL <= 0 || R <= 0 || W <= 0 || P < 0 || hist < 0 || hist + 1 > S_cap ||
         Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0)
         return 1;
+    /* Prompts of request r: rows prompt_cu[r] .. prompt_cu[r+1] of each
+       layer's [prompt_cu[R], Hkv, D] block (each at most P long); without
+       prompt_cu, every request has P rows ([R, P, Hkv, D] per layer). */
+    if (prompt_cu) {
+        if (prompt_cu[0] != 0) return 1;
+        for (int r = 0; r < R; ++r)
+            if (prompt_cu[r + 1] < prompt_cu[r] || prompt_cu[r + 1] - prompt_cu[r] > P) return 1;
+    }
+    const int64_t Tp = prompt_cu ? prompt_cu[R] : (int64_t)R * P;   /* prompt rows per layer */
     const int nkeys = P + hist + 1;
 #pragma omp parallel for collapse(3) schedule(dynamic, 1)
     for (int l = 0; l < NL; ++l)
@@ -236,8 +246,10 @@ int orc_beam_decode_attn(int NL, int R, int W, int P, int hist, int S_cap,
                 for (int h = 0; h < Hq; ++h) {
                     int g = (int)((int64_t)h * Hkv / Hq);
                     int n = 0;
-                    for (int i = 0; i < P; ++i) {
-                        int64_t off = ((((int64_t)l * R + r) * P + i) * Hkv + g) * D;
+                    const int64_t p0 = prompt_cu ? prompt_cu[r] : (int64_t)r * P;
+                    const int Pr = prompt_cu ? prompt_cu[r + 1] - prompt_cu[r] : P;
+                    for (int i = 0; i < Pr; ++i) {
+                        int64_t off = (((int64_t)l * Tp + p0 + i) * Hkv + g) * D;
                         keys[n] = prefix_k + off;
                         vals[n] = prefix_v + off;
                         ++n;

@@ -149,3 +149,59 @@ def test_reorder_identity_and_ancestry():
         for i in range(S_cap - 1, -1, -1):
             assert np.all(wl.bf16_bits_to_f32(state[:, r, j, i]) == 10 * i + anc)
             anc = parents[i][r, anc]
+
+
+def _ragged_case(seed, lengths, NL=2, W=4, hist=2, S_cap=3, Hq=6, Hkv=2, D=16):
+    """Prompts of different lengths packed per layer as [NL, sum(lengths), Hkv, D]."""
+    rng = np.random.default_rng(seed)
+    R = len(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    return dict(
+        q=_rand_bits(rng, (NL, R, W, Hq, D)),
+        pk=_rand_bits(rng, (NL, T, Hkv, D)), pv=_rand_bits(rng, (NL, T, Hkv, D)),
+        sk=_rand_bits(rng, (NL, R, W, S_cap, Hkv, D)), sv=_rand_bits(rng, (NL, R, W, S_cap, Hkv, D)),
+        kn=_rand_bits(rng, (NL, R, W, Hkv, D)), vn=_rand_bits(rng, (NL, R, W, Hkv, D)),
+        parent=rng.integers(0, W, size=(R, W)).astype(np.int32), hist=hist, cu=cu)
+
+
+def test_ragged_prompts_vs_materialised():
+    """Prompts of lengths 0, 1, 7 and 13 in one packed call: each request's
+    result equals the materialised reference of that request alone with its
+    own prompt (an empty prompt leaves only the suffix keys)."""
+    c = _ragged_case(11, [0, 1, 7, 13])
+    scale = 0.3
+    out, sko, svo = oracle.beam_decode_attn(c["q"], c["pk"], c["pv"], c["sk"], c["sv"], c["kn"], c["vn"],
+                                            c["parent"], c["hist"], scale, prompt_cu=c["cu"])
+    cu = c["cu"]
+    for r in range(len(cu) - 1):
+        one = dict(q=c["q"][:, r:r + 1], pk=c["pk"][:, cu[r]:cu[r + 1]][:, None], pv=c["pv"][:, cu[r]:cu[r + 1]][:, None],
+                   sk=c["sk"][:, r:r + 1], sv=c["sv"][:, r:r + 1], kn=c["kn"][:, r:r + 1], vn=c["vn"][:, r:r + 1],
+                   parent=c["parent"][r:r + 1], hist=c["hist"])
+        np.testing.assert_allclose(out[:, r:r + 1], _materialised_reference(one, scale), rtol=1e-11, atol=1e-12)
+    # the suffix reorder does not depend on the prompts
+    dense = oracle.beam_decode_attn(c["q"], np.zeros((2, 4, 1, 2, 16), np.uint16), np.zeros((2, 4, 1, 2, 16), np.uint16),
+                                    c["sk"], c["sv"], c["kn"], c["vn"], c["parent"], c["hist"], scale)
+    assert np.array_equal(sko, dense[1]) and np.array_equal(svo, dense[2])
+
+
+def test_ragged_equal_lengths_is_the_dense_layout():
+    """Equal lengths P packed with offsets r*P are byte for byte the dense
+    [NL, R, P, Hkv, D] layout: identical results."""
+    c = _case(12, R=3, P=9)
+    NL, R, P, Hkv, D = c["pk"].shape
+    cu = (np.arange(R + 1) * P).astype(np.int32)
+    a = oracle.beam_decode_attn(c["q"], c["pk"], c["pv"], c["sk"], c["sv"], c["kn"], c["vn"], c["parent"], c["hist"])
+    b = oracle.beam_decode_attn(c["q"], c["pk"].reshape(NL, R * P, Hkv, D), c["pv"].reshape(NL, R * P, Hkv, D),
+                                c["sk"], c["sv"], c["kn"], c["vn"], c["parent"], c["hist"], prompt_cu=cu)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_ragged_rejects_bad_offsets():
+    c = _ragged_case(13, [2, 3])
+    bad = c["cu"].copy()
+    bad[1] = 6                                     # offsets 0, 6, 5: decreasing
+    with pytest.raises(ValueError):
+        oracle.beam_decode_attn(c["q"], c["pk"], c["pv"], c["sk"], c["sv"], c["kn"], c["vn"], c["parent"], c["hist"],
+                                prompt_cu=bad)
