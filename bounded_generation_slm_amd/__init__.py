@@ -54,7 +54,8 @@ class _BeamAttnArgs(ctypes.Structure):
         "n_heads_q", "n_heads_kv", "head_dim")] + [("scale", ctypes.c_float)] + [
         (n, ctypes.c_void_p) for n in (
             "q", "prefix_k", "prefix_v", "suffix_k_in", "suffix_v_in", "k_new", "v_new", "parent",
-            "suffix_k_out", "suffix_v_out", "out")] + [("out_dtype", ctypes.c_int)]
+            "suffix_k_out", "suffix_v_out", "out")] + [("out_dtype", ctypes.c_int)] + [
+        ("prompt_cu", ctypes.c_void_p), ("prompt_rows", ctypes.c_int32)]
 
 
 _P, _I, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
@@ -233,16 +234,29 @@ def slm_gather_last(ctx: Context, hidden, cu_seqlens, out=None) -> torch.Tensor:
 
 def slm_beam_decode_attn(ctx: Context, q, prefix_k, prefix_v, suffix_k_in, suffix_v_in, k_new, v_new,
                          parent, hist_len: int, suffix_k_out, suffix_v_out, out=None,
-                         scale: Optional[float] = None, out_dtype=torch.float32) -> torch.Tensor:
+                         scale: Optional[float] = None, out_dtype=torch.float32, prompt_cu=None,
+                         prompt_len: Optional[int] = None) -> torch.Tensor:
     """One decode step over all layers.  q [NL,R,W,Hq,D]; prefix_k/v
-    [NL,R,P,Hkv,D]; suffix_*_in/out [NL,R,W,S_cap,Hkv,D]; k_new/v_new
-    [NL,R,W,Hkv,D]; parent [R,W] int32 or None.  Returns out [NL,R,W,Hq,D]."""
+    [NL,R,P,Hkv,D], or with prompt_cu ([R+1] int32 offsets on the device)
+    prompts of different lengths packed per layer as [NL,prompt_cu[R],Hkv,D]
+    with prompt_len their longest length (read from prompt_cu when None);
+    suffix_*_in/out [NL,R,W,S_cap,Hkv,D]; k_new/v_new [NL,R,W,Hkv,D]; parent
+    [R,W] int32 or None.  Returns out [NL,R,W,Hq,D]."""
     dev = ctx.device
     NL, R, W, Hq, D = q.shape
-    P, Hkv = prefix_k.shape[2], prefix_k.shape[3]
     S_cap = suffix_k_out.shape[3]
-    if prefix_k.shape != (NL, R, P, Hkv, D) or prefix_v.shape != prefix_k.shape:
-        raise ValueError("prefix_k/v must be [NL,R,P,Hkv,D]")
+    if prompt_cu is None:
+        P, Hkv = prefix_k.shape[2], prefix_k.shape[3]
+        rows = R * P
+        if prefix_k.shape != (NL, R, P, Hkv, D) or prefix_v.shape != prefix_k.shape:
+            raise ValueError("prefix_k/v must be [NL,R,P,Hkv,D]")
+    else:
+        rows, Hkv = prefix_k.shape[1], prefix_k.shape[2]
+        if tuple(prompt_cu.shape) != (R + 1,):
+            raise ValueError("prompt_cu must be [R+1]")
+        P = int((prompt_cu[1:] - prompt_cu[:-1]).max().item()) if prompt_len is None else int(prompt_len)
+        if prefix_k.shape != (NL, rows, Hkv, D) or prefix_v.shape != prefix_k.shape:
+            raise ValueError("packed prefix_k/v must be [NL,prompt_cu[R],Hkv,D]")
     if k_new.shape != (NL, R, W, Hkv, D) or v_new.shape != k_new.shape:
         raise ValueError("k_new/v_new must be [NL,R,W,Hkv,D]")
     sshape = (NL, R, W, S_cap, Hkv, D)
@@ -269,6 +283,8 @@ def slm_beam_decode_attn(ctx: Context, q, prefix_k, prefix_v, suffix_k_in, suffi
     a.suffix_k_out = _ptr(suffix_k_out, "suffix_k_out", _BF16, dev)
     a.suffix_v_out = _ptr(suffix_v_out, "suffix_v_out", _BF16, dev)
     a.out, a.out_dtype = _ptr(out, "out", tuple(_OUT), dev), _OUT[out.dtype]
+    a.prompt_cu = _ptr(prompt_cu, "prompt_cu", (torch.int32,), dev)
+    a.prompt_rows = rows
     ctx._stream()
     ctx._raise(_lib.slm_beam_decode_attn(ctx._h, ctypes.byref(a)), "slm_beam_decode_attn")
     return out

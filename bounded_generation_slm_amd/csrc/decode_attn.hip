@@ -57,11 +57,6 @@ __global__ __launch_bounds__(NTHR, (D == 64 ? 4 : 2)) void beam_decode_attn_kern
                                                                           int chunks, int chunk_rows) {
     constexpr int NKS = D / 16, NDB = D / 32, KROW = D + 8;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-    const int P = p.prompt_len;
-    const int PP = DecodeLds<D>::p_pad(P);
-    const int VROW = DecodeLds<D>::vrow(P);
-    uint16_t* k_lds = lds;                        // [PP][KROW]
-    uint16_t* vt_lds = lds + (size_t)PP * KROW;   // [D][VROW], keys permuted per 16
     static_assert(!STAGE || !OUT_BF16, "the staged epilogue writes fp32");
 
     const int R = p.num_requests, W = p.width, G = p.group, Hkv = p.n_heads_kv;
@@ -83,10 +78,32 @@ __global__ __launch_bounds__(NTHR, (D == 64 ? 4 : 2)) void beam_decode_attn_kern
     const int n = lane & 31, hf = lane >> 5;
     const int64_t kv_row = (int64_t)Hkv * D;      // elements between consecutive rows
 
+    // This request's prompt: P rows from row prow0 of its layer's prompt block
+    // (layer_rows rows per layer).  Packed prompts of different lengths come
+    // with offsets; offsets that break their rules flag the error and leave
+    // the request without a prompt.
+    int Pr = p.prompt_len;
+    int64_t prow0 = (int64_t)r * Pr, layer_rows = (int64_t)R * Pr;
+    if (p.prompt_cu) {
+        const int a = p.prompt_cu[r], b = p.prompt_cu[r + 1];
+        layer_rows = p.prompt_rows;
+        const bool ok = a >= 0 && b >= a && b <= p.prompt_rows && b - a <= p.prompt_len && (r > 0 || a == 0) &&
+                        (r < R - 1 || b == p.prompt_rows);
+        if (!ok && tid == 0) raise_error(p.err, kErrCuSeqlens);
+        Pr = ok ? b - a : 0;
+        prow0 = ok ? a : 0;
+    }
+    const int P = Pr;
+    const int PP = DecodeLds<D>::p_pad(P);        // within the launch's LDS: P <= prompt_len
+    const int VROW = DecodeLds<D>::vrow(P);
+    uint16_t* k_lds = lds;                        // [PP][KROW]
+    uint16_t* vt_lds = lds + (size_t)PP * KROW;   // [D][VROW], keys permuted per 16
+
     // ---- stage prompt K and V^T of (l, r, g) into LDS ----
     {
-        const uint16_t* pk = p.prefix_k + (int64_t)lr * P * kv_row + (int64_t)g * D;
-        const uint16_t* pv = p.prefix_v + (int64_t)lr * P * kv_row + (int64_t)g * D;
+        const int64_t base = ((int64_t)(lr / R) * layer_rows + prow0) * kv_row + (int64_t)g * D;
+        const uint16_t* pk = p.prefix_k + base;
+        const uint16_t* pv = p.prefix_v + base;
         // K rows in batches of KU chunks per thread: a batch's loads all go out
         // before its LDS writes, so a batch costs one memory round trip
         constexpr int KU = 4;

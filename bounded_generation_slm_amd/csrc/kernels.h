@@ -104,6 +104,8 @@ struct DecodeParams {
     int n_layers, num_requests, width, prompt_len, hist_len, suffix_cap;
     int n_heads_q, n_heads_kv, group;
     float scale_log2;
+    const int32_t* prompt_cu;   // [R+1] offsets of prompts packed per layer, or NULL (each prompt_len rows)
+    int prompt_rows;            // rows per layer of the packed prompts (prompt_cu[R])
 };
 hipError_t launch_beam_decode_attn(const DecodeParams& p, int head_dim, bool out_bf16, int num_cus,
                                    hipStream_t stream);

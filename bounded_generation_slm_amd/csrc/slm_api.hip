@@ -70,6 +70,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3) == 0; }
 
 // Sets the context's device current for the launches that follow.
 slm_status enter(slm_ctx* ctx) {
@@ -198,7 +199,9 @@ slm_status slm_ctx_check(slm_ctx* ctx) {
     if (flag != 0) {
         (void)hipMemset(ctx->err_flag, 0, sizeof(int));
         if (flag == slm::kErrCuSeqlens)
-            return fail(ctx, SLM_ERR_INVALID_ARG, "cu_seqlens: not non-decreasing in [0,T] or a length above max_seqlen");
+            return fail(ctx, SLM_ERR_INVALID_ARG,
+                        "cu_seqlens / prompt_cu: offsets not non-decreasing from 0 to the total, or a length above "
+                        "the maximum");
         if (flag == slm::kErrLabel)
             return fail(ctx, SLM_ERR_INVALID_ARG, "label_head: a label token id outside [0, vocab)");
         if (flag == slm::kErrSelect)
@@ -349,6 +352,10 @@ slm_status slm_beam_decode_attn(slm_ctx* ctx, const slm_beam_attn_args* a) {
         return fail(ctx, SLM_ERR_UNSUPPORTED, "decode: head_dim %d (supported: 64, 128)", a->head_dim);
     if (a->out_dtype != SLM_F32 && a->out_dtype != SLM_BF16) return fail(ctx, SLM_ERR_INVALID_ARG, "decode: unknown out_dtype");
     if (!(a->scale > 0.f) || !std::isfinite(a->scale)) return fail(ctx, SLM_ERR_INVALID_ARG, "decode: bad scale");
+    if (a->prompt_cu && (a->prompt_rows < 0 || (int64_t)a->prompt_rows > (int64_t)a->num_requests * a->prompt_len))
+        return fail(ctx, SLM_ERR_INVALID_ARG, "decode: prompt_rows %d outside [0, num_requests * prompt_len]",
+                    a->prompt_rows);
+    if (a->prompt_cu && !aligned4(a->prompt_cu)) return fail(ctx, SLM_ERR_INVALID_ARG, "decode: prompt_cu must be 4-byte aligned");
     if (!a->q || !a->k_new || !a->v_new || !a->out || !a->suffix_k_out || !a->suffix_v_out ||
         (a->prompt_len > 0 && (!a->prefix_k || !a->prefix_v)) ||
         (a->hist_len > 0 && (!a->suffix_k_in || !a->suffix_v_in)))
@@ -367,11 +374,12 @@ slm_status slm_beam_decode_attn(slm_ctx* ctx, const slm_beam_attn_args* a) {
         W * Hq * D * 4 >= (size_t)INT32_MAX)
         return fail(ctx, SLM_ERR_UNSUPPORTED, "decode: too many rows");
     const size_t qb = NL * R * W * Hq * D * 2, ob = NL * R * W * Hq * D * (a->out_dtype == SLM_F32 ? 4 : 2);
-    const size_t pb = NL * R * a->prompt_len * Hkv * D * 2, sb = NL * R * W * a->suffix_cap * Hkv * D * 2;
+    const size_t prompt_rows = a->prompt_cu ? (size_t)a->prompt_rows : R * a->prompt_len;
+    const size_t pb = NL * prompt_rows * Hkv * D * 2, sb = NL * R * W * a->suffix_cap * Hkv * D * 2;
     const size_t nb = NL * R * W * Hkv * D * 2, parb = R * W * 4;
     struct Buf { const void* p; size_t n; };
     const Buf ins[] = {{a->q, qb}, {a->prefix_k, pb}, {a->prefix_v, pb}, {a->suffix_k_in, sb}, {a->suffix_v_in, sb},
-                       {a->k_new, nb}, {a->v_new, nb}, {a->parent, parb}};
+                       {a->k_new, nb}, {a->v_new, nb}, {a->parent, parb}, {a->prompt_cu, (R + 1) * 4}};
     const Buf outs[] = {{a->out, ob}, {a->suffix_k_out, sb}, {a->suffix_v_out, sb}};
     for (const Buf& o : outs)
         for (const Buf& i : ins)
@@ -388,6 +396,8 @@ slm_status slm_beam_decode_attn(slm_ctx* ctx, const slm_beam_attn_args* a) {
     p.hist_len = a->hist_len; p.suffix_cap = a->suffix_cap; p.n_heads_q = a->n_heads_q;
     p.n_heads_kv = a->n_heads_kv; p.group = a->n_heads_q / a->n_heads_kv;
     p.scale_log2 = a->scale * 1.4426950408889634f;
+    p.prompt_cu = a->prompt_cu;
+    p.prompt_rows = (int)prompt_rows;
     return SLM_LAUNCH(ctx, slm::launch_beam_decode_attn(p, a->head_dim, a->out_dtype == SLM_BF16, ctx->num_cus,
                                                                 ctx->stream),
                       "decode");

@@ -137,9 +137,10 @@ slm_status slm_gather_last(slm_ctx *ctx, const void *hidden, const int32_t *cu_s
  *                rows < hist_len = suffix_in[parent[j]] (bit copy), row
  *                hist_len = k_new/v_new; other rows untouched
  *   out          [NL, R, W, Hq, D]        fp32 or bf16
- * For beam j and query head h (KV head h / (Hq/Hkv)) the keys are the P
- * prompt rows, the hist_len history rows of beam parent[j] and the new row,
- * all visible.  Needs hist_len + 1 <= S_cap, hist_len + 1 <= 8, head_dim 64
+ * For beam j and query head h (KV head h / (Hq/Hkv)) the keys are the
+ * request's prompt rows, the hist_len history rows of beam parent[j] and the
+ * new row, all visible.  prompt_len is the prompt length, or with prompt_cu
+ * (below) the longest prompt.  Needs hist_len + 1 <= S_cap, hist_len + 1 <= 8, head_dim 64
  * or 128, and the prompt K and V^T of one (layer, request, KV head) must fit
  * in one workgroup's LDS (P <= 576 at D = 64, P <= 256 at D = 128), else
  * SLM_ERR_UNSUPPORTED.  Outputs must not overlap any input or each other.
@@ -154,6 +155,15 @@ typedef struct {
     uint16_t *suffix_k_out, *suffix_v_out;
     void *out;
     slm_dtype out_dtype;
+    /* Prompts of different lengths (NULL = every request has prompt_len rows
+     * in the [NL, R, P, Hkv, D] layout above): prompt_cu [R+1] int32 DEVICE
+     * offsets, 0 = prompt_cu[0] <= ... <= prompt_cu[R] = prompt_rows, each
+     * length at most prompt_len; prefix_k/v are then [NL, prompt_rows, Hkv, D]
+     * with request r's prompt at rows prompt_cu[r] .. prompt_cu[r+1] -- the
+     * layout a packed prefill of the R prompts writes.  Offsets that break
+     * these rules set the device error flag (the request then sees no prompt). */
+    const int32_t *prompt_cu;
+    int32_t prompt_rows;
 } slm_beam_attn_args;
 slm_status slm_beam_decode_attn(slm_ctx *ctx, const slm_beam_attn_args *args);
 

@@ -160,6 +160,30 @@ def test_decode_validation(dry):
     assert _status(lambda: dry.beam_decode_attn(hist_len=1, **f)) == slm.SLM_ERR_INVALID_ARG
 
 
+def test_decode_packed_prompts_validation(dry):
+    """Prompts of different lengths packed per layer: prompt_rows (the packed
+    row count) must lie in [0, R * prompt_len]; the packed prompt buffers count
+    in the overlap checks with their real size."""
+    a = _beam_args()
+    NL, Hkv, D = 2, 2, 64
+    cu = torch.tensor([0, 3, 8], dtype=torch.int32)                 # lengths 3 and 5
+    a["prefix_k"], a["prefix_v"] = _bf(NL, 8, Hkv, D), _bf(NL, 8, Hkv, D)
+    assert _status(lambda: dry.beam_decode_attn(hist_len=1, prompt_cu=cu, prompt_len=5, **a)) == slm.SLM_OK
+    assert _status(lambda: dry.beam_decode_attn(hist_len=1, prompt_cu=cu, prompt_len=3, **a)) \
+        == slm.SLM_ERR_INVALID_ARG                                   # 8 rows > R * longest (2 * 3)
+    with pytest.raises(ValueError):                                  # offsets of the wrong length
+        dry.beam_decode_attn(hist_len=1, prompt_cu=cu[:2], prompt_len=5, **a)
+    b = _beam_args()
+    buf = _bf(NL * 8 * Hkv * D + NL * 2 * 3 * 4 * Hkv * D)
+    b["prefix_k"] = buf[:NL * 8 * Hkv * D].view(NL, 8, Hkv, D)
+    b["prefix_v"] = _bf(NL, 8, Hkv, D)
+    b["suffix_k_out"] = buf[NL * 8 * Hkv * D:].view(NL, 2, 3, 4, Hkv, D)   # right after the packed prompt: no overlap
+    assert _status(lambda: dry.beam_decode_attn(hist_len=1, prompt_cu=cu, prompt_len=5, **b)) == slm.SLM_OK
+    b["suffix_k_out"] = buf[NL * 8 * Hkv * D - 64:NL * 8 * Hkv * D - 64 + NL * 2 * 3 * 4 * Hkv * D].view(
+        NL, 2, 3, 4, Hkv, D)                                         # one row into the packed prompt
+    assert _status(lambda: dry.beam_decode_attn(hist_len=1, prompt_cu=cu, prompt_len=5, **b)) == slm.SLM_ERR_ALIAS
+
+
 def test_reorder_and_gather_validation(dry):
     k = _bf(2, 2, 3, 4, 2, 64)
     par = torch.zeros((2, 3), dtype=torch.int32)

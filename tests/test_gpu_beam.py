@@ -180,6 +180,48 @@ def test_reorder_suffix(gpu):
     assert np.all(host_bits(ko)[:, :, :, 4] == 0)           # rows >= rows untouched
 
 
+@pytest.mark.parametrize("lengths,W,hist", [((0, 64, 1, 130, 7), 6, 3), ((480, 33, 200), 4, 2)])
+def test_decode_ragged_prompts(gpu, lengths, W, hist):
+    """Prompts of different lengths packed per layer (offsets prompt_cu): an
+    empty prompt, a whole 64-key chunk, one key, ragged tails; the 8-wave and
+    the 16-wave forms (longest 130 and 480).  History through the parents,
+    suffix bit-exact."""
+    NL, Hq, Hkv, D, S_cap = 2, 14, 2, 64, hist + 1
+    R = len(lengths)
+    note("decode ragged prompts lengths=%s W=%d hist=%d" % (lengths, W, hist))
+    rng = np.random.default_rng(sum(lengths) * 3 + W)
+    bits = lambda *s: wl.f32_to_bf16_bits(rng.standard_normal(s).astype(np.float32))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    q, pk, pv = bits(NL, R, W, Hq, D), bits(NL, T, Hkv, D), bits(NL, T, Hkv, D)
+    sk, sv = bits(NL, R, W, S_cap, Hkv, D), bits(NL, R, W, S_cap, Hkv, D)
+    kn, vn = bits(NL, R, W, Hkv, D), bits(NL, R, W, Hkv, D)
+    par = rng.integers(0, W, size=(R, W)).astype(np.int32)
+    sko = torch.zeros(sk.shape, dtype=torch.bfloat16, device="cuda")
+    svo = torch.zeros_like(sko)
+    out = gpu.beam_decode_attn(dev_bf16(q), dev_bf16(pk), dev_bf16(pv), dev_bf16(sk), dev_bf16(sv), dev_bf16(kn),
+                               dev_bf16(vn), torch.from_numpy(par).cuda(), hist, sko, svo,
+                               prompt_cu=torch.from_numpy(cu).cuda())
+    gpu.check()
+    ref, rk, rv = oracle.beam_decode_attn(q, pk, pv, sk, sv, kn, vn, par, hist, prompt_cu=cu)
+    assert_attn_close(host_f64(out), ref, "decode ragged prompts")
+    n = hist + 1
+    assert np.array_equal(host_bits(sko)[:, :, :, :n], rk[:, :, :, :n])
+    assert np.array_equal(host_bits(svo)[:, :, :, :n], rv[:, :, :, :n])
+
+
+def test_decode_bad_prompt_offsets_are_flagged(gpu):
+    note("decode bad prompt offsets -> device error flag")
+    NL, R, W, Hq, Hkv, D = 1, 2, 2, 4, 2, 64
+    z = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device="cuda")
+    cu = torch.tensor([0, 6, 5], dtype=torch.int32, device="cuda")          # decreasing
+    gpu.beam_decode_attn(z(NL, R, W, Hq, D), z(NL, 5, Hkv, D), z(NL, 5, Hkv, D), None, None, z(NL, R, W, Hkv, D),
+                         z(NL, R, W, Hkv, D), None, 0, z(NL, R, W, 1, Hkv, D), z(NL, R, W, 1, Hkv, D),
+                         prompt_cu=cu, prompt_len=6)
+    with pytest.raises(Exception, match="cu_seqlens|offset|prompt"):
+        gpu.check()
+
+
 def test_bad_parent_is_flagged(gpu):
     note("reorder bad parent -> device error flag")
     k = torch.zeros((1, 1, 4, 2, 1, 64), dtype=torch.bfloat16, device="cuda")
