@@ -6,7 +6,7 @@ contiguity), passes their device pointers and the current HIP stream to the
 C ABI declared in ``include/slm.h``, and raises on a non-OK status.  Every
 step of the computation runs in the HIP kernels of ``libslm.so``; there is no
 CPU or PyTorch fallback, and importing this module fails loudly when the
-library has not been built (``python -m bounded_generation_slm_amd._build``).
+library has not been built (``python bounded_generation_slm_amd/_build.py``).
 
 The functions carry the C names (``slm_packed_prefill_attn`` and so on) and
 take a :class:`Context` first; the same calls are available as methods.
@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libslm.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        "libslm.so is not built; run `python -m bounded_generation_slm_amd._build` "
+        "libslm.so is not built; run `python bounded_generation_slm_amd/_build.py` "
         "(hipcc, gfx950) -- there is no fallback implementation")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -60,6 +60,10 @@ class _BeamAttnArgs(ctypes.Structure):
 
 _P, _I, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
 _lib.slm_abi_version.restype = ctypes.c_int
+_ABI = 3                                  # the struct layouts above
+if _lib.slm_abi_version() != _ABI:
+    raise ImportError("%s has ABI version %d, this binding expects %d: rebuild it with "
+                      "bounded_generation_slm_amd/_build.py" % (LIB_PATH, _lib.slm_abi_version(), _ABI))
 _lib.slm_status_string.restype = ctypes.c_char_p
 _lib.slm_status_string.argtypes = [ctypes.c_int]
 _lib.slm_ctx_create.argtypes = [ctypes.c_int, ctypes.POINTER(_Caps), ctypes.POINTER(_P)]

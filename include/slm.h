@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SLM_ABI_VERSION 2
+#define SLM_ABI_VERSION 3   /* 3: slm_beam_attn_args gained prompt_cu, prompt_rows */
 
 typedef enum {
     SLM_OK = 0,

@@ -13,8 +13,19 @@ sys.path.insert(0, os.path.dirname(__file__))
 import isa_waits  # noqa: E402
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-sys.path.insert(0, ROOT)
-from bounded_generation_slm_amd import _build  # noqa: E402
+
+
+def _load_build_script():
+    # from its file: importing the package would load the built library
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "slm_build_script", os.path.join(ROOT, "bounded_generation_slm_amd", "_build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+_build = _load_build_script()
 
 pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None, reason="hipcc not available")
 
