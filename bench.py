@@ -285,6 +285,43 @@ def extra_workloads(ctx, dev, ev, reps=5):
             "us_per_layer_median": round(us, 1), "us_all_%d_layers" % NL: round(us * NL, 1),
             "hbm_frac": round(pbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         del q, k, v, out
+    # decode (first step) with prompts of different lengths packed with
+    # offsets, as a packed prompt prefill leaves them: the short-prompt beam
+    # shape with lengths U[64, 192] (mean 128)
+    import numpy as np
+    bs = wl.BEAM_SHORT
+    NL, R, W, Hq, Hkv, D = bs.n_layers, bs.num_requests, bs.width, bs.n_heads_q, bs.n_heads_kv, bs.head_dim
+    lengths = np.random.default_rng(bs.base_seed + 77).integers(64, 193, size=R)
+    cu_np = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    Tp = int(cu_np[-1])
+    cu = torch.from_numpy(cu_np).to(dev)
+    q = wl.torch_normal_bf16((NL, R, W, Hq, D), (bs.base_seed, wl.TID_Q, 0, 7), dev)
+    pk = wl.torch_normal_bf16((NL, Tp, Hkv, D), (bs.base_seed, wl.TID_PREFIX_K, 0, 7), dev)
+    pv = wl.torch_normal_bf16((NL, Tp, Hkv, D), (bs.base_seed, wl.TID_PREFIX_V, 0, 7), dev)
+    kn = wl.torch_normal_bf16((NL, R, W, Hkv, D), (bs.base_seed, wl.TID_K_NEW, 0, 7), dev)
+    vn = wl.torch_normal_bf16((NL, R, W, Hkv, D), (bs.base_seed, wl.TID_V_NEW, 0, 7), dev)
+    sko = torch.empty((NL, R, W, bs.suffix_cap, Hkv, D), dtype=torch.bfloat16, device=dev)
+    svo = torch.empty_like(sko)
+    out = torch.empty((NL, R, W, Hq, D), dtype=torch.float32, device=dev)
+    call = lambda: ctx.beam_decode_attn(q, pk, pv, None, None, kn, vn, None, 0, sko, svo, out=out, prompt_cu=cu,
+                                        prompt_len=int(lengths.max()))
+    for _ in range(3):
+        call()
+    times = []
+    for _ in range(reps * 4):
+        e0 = ev()
+        call()
+        times.append((e0, ev()))
+    torch.cuda.synchronize()
+    ctx.check()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in times)[len(times) // 2]
+    nbytes = (NL * R * W * Hq * D * 2 + NL * Tp * Hkv * D * 2 * 2 + 2 * NL * R * W * Hkv * D * 2 * 2
+              + NL * R * W * Hq * D * 4)
+    res["decode_ragged_prompts_" + bs.name] = {
+        "workload": "R%d x W%d, prompt lengths U[64,192] packed with offsets (%d rows), first step, %d layers, "
+                    "Hq%d/Hkv%d/D%d, fp32 out" % (R, W, Tp, NL, Hq, Hkv, D),
+        "us_median": round(us, 1), "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    del q, pk, pv, kn, vn, sko, svo, out
     # the merge on logits (log-softmax folded in) at both beam shapes
     for bs in (wl.BEAM_SHORT, wl.BEAM_LONG):
         R, W, V = bs.num_requests, bs.width, bs.vocab

@@ -437,8 +437,11 @@ __global__ __launch_bounds__(NTHR, (D == 64 ? 4 : 2)) void beam_decode_attn_kern
                     if constexpr (OUT_BF16) {
                         *(u32x2*)((uint16_t*)p.out + qoff + d) = u32x2{pack_bf16x2(r0, r1), pack_bf16x2(r2, r3)};
                     } else {
-                        // never re-read: non-temporal
-                        __builtin_nontemporal_store(f32x4{r0, r1, r2, r3}, (f32x4*)((float*)p.out + qoff + d));
+                        // ordinary stores: these 32-byte pieces of 32 rows
+                        // with the non-temporal hint took the 8-wave form from
+                        // ~130 to ~310 us at prompts of 136-256 rows (the
+                        // 16-wave form measured the same either way)
+                        *(f32x4*)((float*)p.out + qoff + d) = f32x4{r0, r1, r2, r3};
                     }
                 }
         }
