@@ -258,7 +258,10 @@ def slm_beam_decode_attn(ctx: Context, q, prefix_k, prefix_v, suffix_k_in, suffi
         rows, Hkv = prefix_k.shape[1], prefix_k.shape[2]
         if tuple(prompt_cu.shape) != (R + 1,):
             raise ValueError("prompt_cu must be [R+1]")
-        P = int((prompt_cu[1:] - prompt_cu[:-1]).max().item()) if prompt_len is None else int(prompt_len)
+        if prompt_len is None:
+            raise ValueError("prompt_len (the longest prompt) is required with prompt_cu: reading it from the "
+                             "device offsets would synchronise the stream")
+        P = int(prompt_len)
         if prefix_k.shape != (NL, rows, Hkv, D) or prefix_v.shape != prefix_k.shape:
             raise ValueError("packed prefix_k/v must be [NL,prompt_cu[R],Hkv,D]")
     if k_new.shape != (NL, R, W, Hkv, D) or v_new.shape != k_new.shape:
@@ -351,6 +354,8 @@ def slm_beam_reorder_suffix(ctx: Context, parent, k_in, v_in, rows: int, k_out, 
     for name, t in (("v_in", v_in), ("k_out", k_out), ("v_out", v_out)):
         if t.shape != k_in.shape:
             raise ValueError("%s must match k_in's shape" % name)
+    if tuple(parent.shape) != (R, W):
+        raise ValueError("parent must be [R, W] = %s" % ((R, W),))
     ctx._stream()
     rc = _lib.slm_beam_reorder_suffix(
         ctx._h, NL, R, W, int(rows), S_cap, Hkv, D, _ptr(parent, "parent", (torch.int32,), dev),
@@ -378,6 +383,14 @@ def slm_label_head(ctx: Context, hidden, cu_seqlens, lm_head, labels, k: int, la
                torch.empty((B, K), dtype=torch.float32, device=dev),
                torch.empty((B, K), dtype=torch.int32, device=dev))
     lg, pr, ti, tp, tc = out
+    if label_map is not None and label_map.numel() != L:
+        raise ValueError("label_map must hold one class per label (%d)" % L)
+    for name, t, shp in (("logits", lg, (B, L)), ("probs", pr, (B, L)), ("top_idx", ti, (B, K)),
+                         ("top_prob", tp, (B, K)), ("top_class", tc, (B, K))):
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError("%s must be %s" % (name, shp))
+    if lg is None or ti is None or tp is None:
+        raise ValueError("logits, top_idx and top_prob are required outputs")
     ctx._stream()
     rc = _lib.slm_label_head(
         ctx._h, _ptr(hidden, "hidden", _BF16, dev), _ptr(cu_seqlens, "cu_seqlens", (torch.int32,), dev), B, T, H,

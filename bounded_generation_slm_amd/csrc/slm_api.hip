@@ -228,7 +228,9 @@ slm_status slm_packed_prefill_attn(slm_ctx* ctx, const uint16_t* q, const uint16
     if (!(scale > 0.f) || !std::isfinite(scale))
         return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: scale must be finite and positive");
     if (!cu_seqlens) return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: cu_seqlens is NULL");
-    if (total_tokens == 0 || num_seqs == 0 || max_seqlen == 0) return ok(ctx);
+    if (max_seqlen == 0 && total_tokens > 0)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: max_seqlen 0 with %d packed tokens", total_tokens);
+    if (total_tokens == 0 || num_seqs == 0) return ok(ctx);
     if (!q || !k || !v || !out) return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: NULL tensor");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: tensors must be 16-byte aligned");

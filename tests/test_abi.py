@@ -197,3 +197,37 @@ def test_reorder_and_gather_validation(dry):
     cu = torch.tensor([0, 4, 10], dtype=torch.int32)
     assert _status(lambda: dry.gather_last(hidden, cu)) == slm.SLM_OK
     assert _status(lambda: dry.gather_last(hidden, cu, out=hidden[:2])) == slm.SLM_ERR_ALIAS
+
+
+def test_shape_checks_before_the_call(dry):
+    """Caller-supplied buffers whose shapes the C side trusts are checked by
+    the binding: undersized outputs, a label map of the wrong length, parents
+    of the wrong shape, and prompt offsets without the longest length."""
+    hidden, lm = _bf(10, 64), _bf(50, 64)
+    cu = torch.tensor([0, 3, 10], dtype=torch.int32)
+    labels = torch.arange(8, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        dry.label_head(hidden, cu, lm, labels, 3, label_map=torch.arange(7, dtype=torch.int32))
+    good = (torch.zeros((2, 8)), torch.zeros((2, 8)), torch.zeros((2, 3), dtype=torch.int32), torch.zeros((2, 3)),
+            torch.zeros((2, 3), dtype=torch.int32))
+    assert _status(lambda: dry.label_head(hidden, cu, lm, labels, 3, out=good)) == slm.SLM_OK
+    for i, shp in enumerate(((2, 7), (1, 8), (2, 2), (2, 2), (1, 3))):
+        bad = list(good)
+        bad[i] = torch.zeros(shp, dtype=good[i].dtype)
+        with pytest.raises(ValueError):
+            dry.label_head(hidden, cu, lm, labels, 3, out=tuple(bad))
+    k = _bf(2, 2, 3, 4, 2, 64)
+    with pytest.raises(ValueError):
+        dry.beam_reorder_suffix(torch.zeros((2, 2), dtype=torch.int32), k, k.clone(), 2, _bf(2, 2, 3, 4, 2, 64),
+                                _bf(2, 2, 3, 4, 2, 64))
+    a = _beam_args()
+    a["prefix_k"], a["prefix_v"] = _bf(2, 8, 2, 64), _bf(2, 8, 2, 64)
+    with pytest.raises(ValueError):
+        dry.beam_decode_attn(hist_len=1, prompt_cu=torch.tensor([0, 3, 8], dtype=torch.int32), **a)
+
+
+def test_prefill_max_seqlen_zero_with_tokens(dry):
+    """A pack with tokens but max_seqlen 0 is rejected, not silently skipped."""
+    q, k, v = _bf(10, 4, 64), _bf(10, 2, 64), _bf(10, 2, 64)
+    cu = torch.tensor([0, 3, 10], dtype=torch.int32)
+    assert _status(lambda: dry.packed_prefill_attn(q, k, v, cu, 0)) == slm.SLM_ERR_INVALID_ARG

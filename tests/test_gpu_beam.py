@@ -201,7 +201,7 @@ def test_decode_ragged_prompts(gpu, lengths, W, hist):
     svo = torch.zeros_like(sko)
     out = gpu.beam_decode_attn(dev_bf16(q), dev_bf16(pk), dev_bf16(pv), dev_bf16(sk), dev_bf16(sv), dev_bf16(kn),
                                dev_bf16(vn), torch.from_numpy(par).cuda(), hist, sko, svo,
-                               prompt_cu=torch.from_numpy(cu).cuda())
+                               prompt_cu=torch.from_numpy(cu).cuda(), prompt_len=max(lengths))
     gpu.check()
     ref, rk, rv = oracle.beam_decode_attn(q, pk, pv, sk, sv, kn, vn, par, hist, prompt_cu=cu)
     assert_attn_close(host_f64(out), ref, "decode ragged prompts")
