@@ -55,9 +55,10 @@ def _load():
         lib.orc_topk_merge_logits.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P]
         lib.orc_label_head.argtypes = [P, P, i32, i32, P, i32, P, i32, i32, P, P, P, P, P, P]
         lib.orc_reorder_suffix.argtypes = [i32] * 7 + [P] * 5
+        lib.orc_beam_backtrack.argtypes = [P, P, i32, i32, i32, P]
         for f in ("orc_prefill_attn", "orc_prefill_attn_rows", "orc_gather_last",
                   "orc_beam_decode_attn", "orc_topk_merge", "orc_topk_merge_logits", "orc_label_head",
-                  "orc_reorder_suffix"):
+                  "orc_reorder_suffix", "orc_beam_backtrack"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -216,17 +217,36 @@ def reorder_suffix(parent, k_in, v_in, rows):
     return ko, vo
 
 
+def beam_backtrack(tokens, parent):
+    """tokens, parent [n_merges, R, W] int32 (the merges' outputs, merge 0
+    first) -> seq [R, W, n_merges]: the token each final beam's ancestor took
+    at every merge, found by following the parents back from the last merge."""
+    tok, par = _c(tokens, np.int32), _c(parent, np.int32)
+    n, R, W = tok.shape
+    if par.shape != tok.shape:
+        raise ValueError("beam_backtrack: tokens and parent shapes differ")
+    seq = np.empty((R, W, n), np.int32)
+    _check(_load().orc_beam_backtrack(_p(tok), _p(par), n, R, W, _p(seq)), "beam_backtrack")
+    return seq
+
+
 def beam_search(step_inputs, prefix_k, prefix_v, logprobs_by_step, width, n_steps,
-                suffix_cap=None, scale=None):
+                suffix_cap=None, scale=None, on_step=None):
     """The fixed-step sequence: merge on the prefill log-probs (one beam in),
     then for t = 1..n_steps: decode attention with s = t suffix rows (history
     read through the last merge's parents), then the merge on step t's
-    log-probs.  ``step_inputs(t)`` returns dict(q, k_new, v_new) for step t;
+    log-probs; finally the suffix reordered by the last parents and the
+    backtrack of the parents into each final beam's token sequence.
+    ``step_inputs(t)`` returns dict(q, k_new, v_new) for step t;
     ``logprobs_by_step(t)`` the [R,Win,V] log-probs.
 
     Returns a dict with per-step outputs: tokens/parent/cum lists (index 0 is
-    the first merge), attention outputs and suffix states per step, and the
-    final suffix reordered by the last merge's parents."""
+    the first merge), attention outputs and suffix states per step, the final
+    suffix reordered by the last merge's parents, and ``sequences`` [R,W,N+1].
+    With ``on_step``, each decode step's results are handed to
+    ``on_step(t, dict(attn, suffix_k, suffix_v))`` instead of being kept (the
+    attention outputs of a full-size search would not fit host memory
+    comfortably)."""
     lp0 = logprobs_by_step(0)
     R = lp0.shape[0]
     cum0 = np.zeros((R, lp0.shape[1]), np.float32)
@@ -241,13 +261,18 @@ def beam_search(step_inputs, prefix_k, prefix_v, logprobs_by_step, width, n_step
         x = step_inputs(t)
         out, sk, sv = beam_decode_attn(x["q"], prefix_k, prefix_v, sk, sv, x["k_new"],
                                        x["v_new"], par, t - 1, scale)
-        res["attn"].append(out)
-        res["suffix_k"].append(sk)
-        res["suffix_v"].append(sv)
+        if on_step is None:
+            res["attn"].append(out)
+            res["suffix_k"].append(sk)
+            res["suffix_v"].append(sv)
+        else:
+            on_step(t, dict(attn=out, suffix_k=sk, suffix_v=sv))
+        del out
         tok, par, cum = topk_merge(logprobs_by_step(t), cum, width)
         res["tokens"].append(tok)
         res["parent"].append(par)
         res["cum"].append(cum)
     fk, fv = reorder_suffix(par, sk, sv, n_steps)
     res["final_suffix_k"], res["final_suffix_v"] = fk, fv
+    res["sequences"] = beam_backtrack(np.stack(res["tokens"]), np.stack(res["parent"]))
     return res

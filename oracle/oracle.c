@@ -433,3 +433,31 @@ int orc_reorder_suffix(int NL, int R, int W, int rows, int S_cap, int Hkv, int D
             }
     return 0;
 }
+
+/* Final backtrack of a fixed-step beam search into token sequences (the
+ * request returns its candidate sequences: page "SLM 生成式高并发推理引擎：延迟
+ * 约束下的有效吞吐优化", §1.1, beam-search form).  tokens and parent hold the
+ * outputs of the n_merges merges, [n_merges, R, W] each (merge 0 takes one
+ * beam in, so its parents are 0).  Beam j after the last merge emitted
+ * tokens[n_merges-1][r][j] and descends from beam parent[n_merges-1][r][j] of
+ * the merge before; following the parents back to merge 0 gives one token
+ * per merge.  seq [R, W, n_merges]: seq[r][j][t] = the token beam j's
+ * ancestor took at merge t.  A parent outside [0, W) is rejected. */
+int orc_beam_backtrack(const int32_t *tokens, const int32_t *parent, int n_merges, int R,
+                       int W, int32_t *seq)
+{
+    if (n_merges <= 0 || R <= 0 || W <= 0)
+        return 1;
+    for (int r = 0; r < R; ++r)
+        for (int j = 0; j < W; ++j) {
+            int b = j;                                  /* beam index at merge t */
+            for (int t = n_merges - 1; t >= 0; --t) {
+                const int64_t at = ((int64_t)t * R + r) * W + b;
+                seq[((int64_t)r * W + j) * n_merges + t] = tokens[at];
+                b = parent[at];
+                if (t > 0 && (b < 0 || b >= W))
+                    return 1;
+            }
+        }
+    return 0;
+}
