@@ -38,7 +38,7 @@ EXPORTED = (
     "slm_abi_version", "slm_status_string", "slm_ctx_create", "slm_ctx_destroy",
     "slm_ctx_set_stream", "slm_ctx_check", "slm_ctx_last_error", "slm_packed_prefill_attn",
     "slm_gather_last", "slm_beam_decode_attn", "slm_beam_topk_merge", "slm_beam_topk_merge_logits",
-    "slm_beam_reorder_suffix", "slm_label_head",
+    "slm_beam_reorder_suffix", "slm_label_head", "slm_beam_backtrack",
 )
 
 
@@ -60,7 +60,7 @@ class _BeamAttnArgs(ctypes.Structure):
 
 _P, _I, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
 _lib.slm_abi_version.restype = ctypes.c_int
-_ABI = 3                                  # the struct layouts above
+_ABI = 4                                  # the struct layouts above and the symbol set
 if _lib.slm_abi_version() != _ABI:
     raise ImportError("%s has ABI version %d, this binding expects %d: rebuild it with "
                       "bounded_generation_slm_amd/_build.py" % (LIB_PATH, _lib.slm_abi_version(), _ABI))
@@ -80,9 +80,10 @@ _lib.slm_beam_topk_merge.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]
 _lib.slm_beam_topk_merge_logits.argtypes = [_P, _P, ctypes.c_int, _P, _I, _I, _I, _I, _P, _P, _P, _P]
 _lib.slm_label_head.argtypes = [_P, _P, _P, _I, _I, _I, _P, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P]
 _lib.slm_beam_reorder_suffix.argtypes = [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
+_lib.slm_beam_backtrack.argtypes = [_P, _P, _P, _I, _I, _I, _P]
 for _name in ("slm_ctx_create", "slm_ctx_set_stream", "slm_ctx_check", "slm_packed_prefill_attn",
               "slm_gather_last", "slm_beam_decode_attn", "slm_beam_topk_merge", "slm_beam_topk_merge_logits",
-              "slm_beam_reorder_suffix", "slm_label_head"):
+              "slm_beam_reorder_suffix", "slm_label_head", "slm_beam_backtrack"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -186,6 +187,9 @@ class Context:
 
     def beam_reorder_suffix(self, parent, k_in, v_in, rows: int, k_out, v_out):
         return slm_beam_reorder_suffix(self, parent, k_in, v_in, rows, k_out, v_out)
+
+    def beam_backtrack(self, tokens, parent, out=None):
+        return slm_beam_backtrack(self, tokens, parent, out)
 
     def label_head(self, hidden, cu_seqlens, lm_head, labels, k: int, label_map=None, probs: bool = True,
                    out=None):
@@ -400,3 +404,21 @@ def slm_label_head(ctx: Context, hidden, cu_seqlens, lm_head, labels, k: int, la
         _ptr(tp, "top_prob", (torch.float32,), dev), _ptr(tc, "top_class", (torch.int32,), dev))
     ctx._raise(rc, "slm_label_head")
     return lg, pr, ti, tp, tc
+
+
+def slm_beam_backtrack(ctx: Context, tokens, parent, out=None) -> torch.Tensor:
+    """tokens, parent [n_merges,R,W] int32 (the merges' outputs in order) -> sequences [R,W,n_merges] int32:
+    the token each final beam's ancestor took at every merge."""
+    dev = ctx.device
+    if tokens.dim() != 3 or tuple(parent.shape) != tuple(tokens.shape):
+        raise ValueError("tokens and parent must both be [n_merges, R, W]")
+    n, R, W = tokens.shape
+    out = torch.empty((R, W, n), dtype=torch.int32, device=dev) if out is None else out
+    if tuple(out.shape) != (R, W, n):
+        raise ValueError("out must be [R, W, n_merges]")
+    ctx._stream()
+    rc = _lib.slm_beam_backtrack(ctx._h, _ptr(tokens, "tokens", (torch.int32,), dev),
+                                 _ptr(parent, "parent", (torch.int32,), dev), n, R, W,
+                                 _ptr(out, "out", (torch.int32,), dev))
+    ctx._raise(rc, "slm_beam_backtrack")
+    return out

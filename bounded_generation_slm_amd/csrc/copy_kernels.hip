@@ -1,11 +1,15 @@
-// Pure data movement on the hot path: last-valid-token gather and the
-// parent-indexed suffix K/V reorder.  Both are bit copies.
+// Pure data movement on the hot path: last-valid-token gather, the
+// parent-indexed suffix K/V reorder and the final backtrack of the parents
+// into token sequences.  All are bit copies.
 //
 // Gather (page "SLM 生成式高并发推理引擎：延迟约束下的有效吞吐优化", §1.1): a
 // prefill-only request reads its result at each sequence's last valid token,
 // so only B rows, not T, reach the head that follows.
 // Reorder (same page, §1.1 parent index, §1.2 per-beam suffix K/V): after a
 // merge every beam takes its parent's suffix rows.
+// Backtrack (same page, §1.1: a beam-search request returns a few candidate
+// sequences): after the last merge every beam follows its parents back to
+// the first merge, one token per merge.
 #include "common.h"
 #include "kernels.h"
 
@@ -53,7 +57,38 @@ __global__ __launch_bounds__(256) void reorder_suffix_kernel(const ReorderParams
     *(u32x4*)(p.v_out + dst_off) = *(const u32x4*)(p.v_in + src_off);
 }
 
+// One lane per final beam (r, j): its sequence is written from the last
+// merge back to the first.  The [n, R, W] inputs are read a step at a time,
+// each step by the W lanes of a request at once; the [R, W, n] output row of a
+// beam is contiguous.  A parent outside [0, W) flags the error and leaves the
+// earlier entries of that sequence at -1.
+__global__ __launch_bounds__(256) void backtrack_kernel(const BacktrackParams p) {
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= (int64_t)p.num_requests * p.width) return;
+    const int r = (int)(id / p.width);
+    int b = (int)(id % p.width);
+    int32_t* out = p.seq + id * p.n_merges;
+    for (int t = p.n_merges - 1; t >= 0; --t) {
+        const int64_t at = ((int64_t)t * p.num_requests + r) * p.width + b;
+        out[t] = p.tokens[at];
+        const int nb = p.parent[at];
+        if (t > 0 && (nb < 0 || nb >= p.width)) {
+            raise_error(p.err, kErrParent);
+            for (int u = t - 1; u >= 0; --u) out[u] = -1;
+            return;
+        }
+        b = nb;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_backtrack(const BacktrackParams& p, hipStream_t stream) {
+    const int64_t n = (int64_t)p.num_requests * p.width;
+    if (n == 0 || p.n_merges == 0) return hipSuccess;
+    hipLaunchKernelGGL(backtrack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_gather_last(const GatherParams& p, hipStream_t stream) {
     if (p.num_seqs == 0) return hipSuccess;

@@ -88,6 +88,15 @@ struct ReorderParams {
 };
 hipError_t launch_reorder_suffix(const ReorderParams& p, hipStream_t stream);
 
+struct BacktrackParams {
+    const int32_t* tokens;              // [n_merges, R, W]
+    const int32_t* parent;              // [n_merges, R, W]
+    int32_t* seq;                       // [R, W, n_merges]
+    int* err;
+    int n_merges, num_requests, width;
+};
+hipError_t launch_backtrack(const BacktrackParams& p, hipStream_t stream);
+
 struct DecodeParams {
     const uint16_t* q;
     const uint16_t* prefix_k;

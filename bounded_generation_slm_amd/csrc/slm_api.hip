@@ -546,4 +546,25 @@ slm_status slm_beam_reorder_suffix(slm_ctx* ctx, int32_t n_layers, int32_t num_r
     return SLM_LAUNCH(ctx, slm::launch_reorder_suffix(p, ctx->stream), "reorder");
 }
 
+slm_status slm_beam_backtrack(slm_ctx* ctx, const int32_t* tokens, const int32_t* parent, int32_t n_merges,
+                              int32_t num_requests, int32_t width, int32_t* sequences) {
+    slm_status s = enter(ctx);
+    if (s != SLM_OK) return s;
+    if (n_merges <= 0 || num_requests < 0 || width <= 0)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "backtrack: a size is out of range");
+    if ((int64_t)n_merges * num_requests * width > INT32_MAX)
+        return fail(ctx, SLM_ERR_UNSUPPORTED, "backtrack: more than 2^31 - 1 entries");
+    if (num_requests == 0) return ok(ctx);
+    if (!tokens || !parent || !sequences) return fail(ctx, SLM_ERR_INVALID_ARG, "backtrack: NULL tensor");
+    if (!aligned4(tokens) || !aligned4(parent) || !aligned4(sequences))
+        return fail(ctx, SLM_ERR_INVALID_ARG, "backtrack: tensors must be 4-byte aligned");
+    const size_t nb = (size_t)n_merges * num_requests * width * 4;
+    if (overlaps(sequences, nb, tokens, nb) || overlaps(sequences, nb, parent, nb))
+        return fail(ctx, SLM_ERR_ALIAS, "backtrack: sequences overlap an input");
+    slm::BacktrackParams p{};
+    p.tokens = tokens; p.parent = parent; p.seq = sequences; p.err = ctx->err_flag;
+    p.n_merges = n_merges; p.num_requests = num_requests; p.width = width;
+    return SLM_LAUNCH(ctx, slm::launch_backtrack(p, ctx->stream), "backtrack");
+}
+
 }  // extern "C"

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SLM_ABI_VERSION 3   /* 3: slm_beam_attn_args gained prompt_cu, prompt_rows */
+#define SLM_ABI_VERSION 4   /* 3: slm_beam_attn_args gained prompt_cu, prompt_rows; 4: slm_beam_backtrack */
 
 typedef enum {
     SLM_OK = 0,
@@ -255,6 +255,26 @@ slm_status slm_beam_reorder_suffix(slm_ctx *ctx, int32_t n_layers, int32_t num_r
                                    int32_t n_heads_kv, int32_t head_dim,
                                    const int32_t *parent, const uint16_t *k_in,
                                    const uint16_t *v_in, uint16_t *k_out, uint16_t *v_out);
+
+/*
+ * Final backtrack of a fixed-step beam search into its candidate sequences
+ * (§1.1: a beam-search request returns a few candidate sequences; parent
+ * indices carry the beams from merge to merge).
+ *   tokens, parent [n_merges, R, W] int32 (device): the outputs of the
+ *                n_merges merges in order; merge 0 took one beam in, so its
+ *                parents are not read
+ *   sequences    [R, W, n_merges] int32 (device): sequences[r][j][t] is the
+ *                token that final beam j's ancestor took at merge t
+ * Beam j after the last merge emitted tokens[n_merges-1][r][j]; its parent
+ * there names the beam of the merge before, and so on back to merge 0.  The
+ * beams keep the last merge's order (its cum_out holds their scores).  A
+ * parent outside [0, W) at merges 1.. sets the device error flag and leaves
+ * the earlier entries of that sequence at -1.  sequences must not overlap the
+ * inputs.  One lane per final beam; the call reads n_merges * R * W * 8
+ * bytes and writes R * W * n_merges * 4.
+ */
+slm_status slm_beam_backtrack(slm_ctx *ctx, const int32_t *tokens, const int32_t *parent, int32_t n_merges,
+                              int32_t num_requests, int32_t width, int32_t *sequences);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert declared == set(slm.EXPORTED)
-    assert slm.abi_version() == 3
+    assert slm.abi_version() == 4
 
 
 @pytest.fixture
@@ -231,3 +231,17 @@ def test_prefill_max_seqlen_zero_with_tokens(dry):
     q, k, v = _bf(10, 4, 64), _bf(10, 2, 64), _bf(10, 2, 64)
     cu = torch.tensor([0, 3, 10], dtype=torch.int32)
     assert _status(lambda: dry.packed_prefill_attn(q, k, v, cu, 0)) == slm.SLM_ERR_INVALID_ARG
+
+
+def test_backtrack_validation(dry):
+    tok = torch.zeros((3, 2, 4), dtype=torch.int32)
+    par = torch.zeros((3, 2, 4), dtype=torch.int32)
+    assert _status(lambda: dry.beam_backtrack(tok, par)) == slm.SLM_OK
+    with pytest.raises(ValueError):
+        dry.beam_backtrack(tok, par[:2])
+    with pytest.raises(ValueError):
+        dry.beam_backtrack(tok, par, out=torch.zeros((2, 4, 2), dtype=torch.int32))
+    buf = torch.zeros(3 * 2 * 4 * 2, dtype=torch.int32)
+    assert _status(lambda: dry.beam_backtrack(buf[:24].view(3, 2, 4), par, out=buf[12:36].view(2, 4, 3))) \
+        == slm.SLM_ERR_ALIAS
+    assert _status(lambda: dry.beam_backtrack(tok[:0], par[:0])) == slm.SLM_ERR_INVALID_ARG   # no merge
