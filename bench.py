@@ -9,14 +9,18 @@ resident in HBM:
     [T,1024] bf16 hidden state;
   * short-prompt beam search: 32 requests x 100 beams, prompt 128, 4 fixed
     decode steps over 24 layers (14 query / 2 KV heads, head_dim 64), vocab
-    151,936: first merge (one beam in), then per step the 24-layer decode
-    attention (history read through the last parents, suffix written in the
-    new order) and the top-k merge; finally the suffix reorder by the last
-    parents.
+    151,936, as one call of the library's fixed-step driver: first merge (one
+    beam in), then per step the 24-layer decode attention (history read
+    through the last parents, suffix written in the new order) and the top-k
+    merge; finally the suffix reorder by the last parents and the backtrack
+    of the parents into each beam's token sequence.
 
 value = prefill tokens per step (T, each through all 28 layers) / step time.
-The JSON line also carries the per-part times, the roofline of the dominant
-kernel (packed prefill attention) and the oracle timed on a bounded sample.
+The JSON line also carries the per-part times (medians; the beam-search
+breakdown from a pass that issues the same launches one by one with events
+between them), the roofline of the dominant kernel (packed prefill
+attention, from the mean of its per-launch events over the timed steps) and
+the oracle timed per workload on the same arrays.
 Outside the timed step, the same calls are timed on two more workloads for
 reporting only: one prefill-only request (15 packed samples, one layer, then
 the gather) and the long-prompt wide beam search (8 requests x 400 beams,
@@ -46,7 +50,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the timed oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the timed oracle runs")
+    ap.add_argument("--cpu-baseline-full", action="store_true",
+                    help="also time the oracle's whole long-prompt search (about a minute more)")
     ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph timing of the step")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the reporting-only prefill-request and long-prompt beam timings")
@@ -107,50 +113,72 @@ def one_thread_times():
         return {"error": str(e)[:200]}
 
 
-def cpu_baseline(pf, bs):
-    """The oracle on a bounded sample of the same workload (roughly 10 s on 16
-    host threads), scaled to the whole step: one whole prefill layer (all 960
-    sequences), one layer of each decode step, and 8 requests of each merge."""
+def _host(t):
+    """A device tensor's contents on the host (bf16 as its 16-bit storage)."""
+    import numpy as np
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def oracle_beam_search_time(run):
+    """The oracle's whole fixed-step search (oracle.beam_search: every merge,
+    every decode step over all layers, the final reorder and backtrack) on
+    host copies of the bench's device inputs; seconds."""
+    import oracle
+    x, bs = run.x, run.bs
+    pk, pv = _host(x["prefix_k"]), _host(x["prefix_v"])
+    steps = {t: dict(q=_host(x["q"][t - 1]), k_new=_host(x["k_new"][t - 1]), v_new=_host(x["v_new"][t - 1]))
+             for t in range(1, bs.n_steps + 1)}
+    lps = [_host(lp) for lp in x["logprobs"]]
+    t0 = time.perf_counter()
+    oracle.beam_search(steps.__getitem__, pk, pv, lps.__getitem__, bs.width, bs.n_steps,
+                       on_step=lambda t, r: None)
+    return round(time.perf_counter() - t0, 3)
+
+
+def cpu_baseline(pf, pf_dev, beam):
+    """The oracle on the host cores, per workload on the same arrays the GPU
+    reads: the tiny workload (prefill and 4-step search), the one-request
+    prefill, layer 0 of the 960-sequence pack (the 28 layer calls of a step
+    read one Q/K/V set, so the step's prefill is 28 times that) and the whole
+    short-prompt search.  value: prefill tokens per second of one whole step
+    (28 prefill layers + gather + short-prompt search), like the GPU value."""
     import numpy as np
 
     import oracle
     import workloads as wl
 
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    L = list(pf.lengths)
-    sub = L
-    shp = wl.PrefillShape("sample", pf.base_seed, tuple(sub), pf.n_heads_q, pf.n_heads_kv, pf.head_dim)
-    x = wl.prefill_inputs(shp)
+    per = {}
+    x = wl.prefill_inputs(wl.TINY_PREFILL)
     t0 = time.perf_counter()
     oracle.prefill_attn(x["q"], x["k"], x["v"], x["cu_seqlens"])
-    t_pre = time.perf_counter() - t0
-    pairs = lambda ls: sum(l * (l + 1) for l in ls)
-    est = t_pre * pairs(L) / pairs(sub) * pf.n_layers
-
-    st = wl.beam_static_inputs(bs, layers=[0])
-    hist_rng = np.random.default_rng(0)
-    t_dec = 0.0
-    for t in range(1, bs.n_steps + 1):
-        xs = wl.beam_step_inputs(bs, t, layers=[0])
-        shp6 = (1, bs.num_requests, bs.width, bs.suffix_cap, bs.n_heads_kv, bs.head_dim)
-        sk = wl.f32_to_bf16_bits(hist_rng.standard_normal(shp6).astype(np.float32))
-        par = hist_rng.integers(0, bs.width, size=(bs.num_requests, bs.width)).astype(np.int32)
-        t0 = time.perf_counter()
-        oracle.beam_decode_attn(xs["q"], st["prefix_k"], st["prefix_v"], sk, sk, xs["k_new"], xs["v_new"], par, t - 1)
-        t_dec += time.perf_counter() - t0
-    est += t_dec * bs.n_layers
-
-    r_s = 8
-    t_top = 0.0
-    for t in range(0, bs.n_steps + 1):
-        win = 1 if t == 0 else bs.width
-        lp = wl.logprobs(bs.base_seed, (r_s, win, bs.vocab), t)
-        cum = np.zeros((r_s, win), np.float32)
-        t0 = time.perf_counter()
-        oracle.topk_merge(lp, cum, bs.width)
-        t_top += time.perf_counter() - t0
-    est += t_top * bs.num_requests / r_s
-    sampled = t_pre + t_dec + t_top
+    tb = wl.TINY_BEAM
+    st = wl.beam_static_inputs(tb)
+    oracle.beam_search(lambda t: wl.beam_step_inputs(tb, t), st["prefix_k"], st["prefix_v"],
+                       lambda t: wl.beam_logprobs(tb, t), tb.width, tb.n_steps)
+    per["tiny (prefill pack of 4 + 4-step search, R2 x W4, V1000)"] = round(time.perf_counter() - t0, 3)
+    x = wl.prefill_inputs(wl.PREFILL_REQUEST)
+    t0 = time.perf_counter()
+    oracle.prefill_attn(x["q"], x["k"], x["v"], x["cu_seqlens"])
+    oracle.gather_last(x["hidden"], x["cu_seqlens"])
+    per["prefill_request (15 sequences, 1 layer + gather)"] = round(time.perf_counter() - t0, 3)
+    q, k, v, hidden = (_host(t) for t in pf_dev)
+    cu = pf.cu_seqlens()
+    t0 = time.perf_counter()
+    oracle.prefill_attn(q, k, v, cu)
+    t_layer = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.gather_last(hidden, cu)
+    t_gather = time.perf_counter() - t0
+    del q, k, v, hidden
+    per["prefill_throughput layer 0 (960 sequences, T=%d)" % pf.total_tokens] = round(t_layer, 3)
+    per["prefill_throughput 28 layers (extrapolated: 28 x layer 0)"] = round(t_layer * pf.n_layers, 3)
+    t_search = oracle_beam_search_time(beam)
+    per["beam_short_prompt whole search (R32 x W100, 4 steps, 24 layers)"] = t_search
+    step_s = t_layer * pf.n_layers + t_gather + t_search
     cpu_model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -161,16 +189,17 @@ def cpu_baseline(pf, bs):
     except OSError:
         pass
     return {
-        "value": pf.total_tokens / est,
+        "value": pf.total_tokens / step_s,
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
+        "per_workload_s": per,
         "host": {"cpu_model": cpu_model, "logical_cpus": os.cpu_count(), "omp_threads": threads,
                  "one_thread_s": one_thread_times()},
-        "sample": ("fp64 C oracle, %d threads: prefill layer 0 over %d of 960 sequences (%d tokens), "
-                   "decode layer 0 of each of the 4 steps, top-k merge of 8 of 32 requests for the 5 merges; "
-                   "%.1f s measured, scaled by causal pairs / layers / requests to one whole step "
-                   "(%.0f s estimated)" % (threads, len(sub), sum(sub), sampled, est)),
+        "sample": ("fp64 C oracle, %d threads, on the bench's own arrays: prefill layer 0 of the 960-sequence pack "
+                   "in full (%.1f s, x28 for the step's 28 layer calls over the same Q/K/V), the gather, and the whole "
+                   "short-prompt search in full (%.1f s); one step estimated at %.0f s" % (
+                       threads, t_layer, t_search, step_s)),
     }
 
 
@@ -186,7 +215,7 @@ def traffic_from_counters(kernel_file: str, launch_bytes_key: str):
     return rec.get(launch_bytes_key)
 
 
-def extra_workloads(ctx, dev, ev, reps=5):
+def extra_workloads(ctx, dev, ev, reps=5, full_cpu=False):
     """Reporting-only timings outside the timed step (not part of value)."""
     import torch
     import workloads as wl
@@ -246,17 +275,12 @@ def extra_workloads(ctx, dev, ev, reps=5):
     del lm, hid_pf
     del q, k, v, hidden, out
     # the long-prompt wide beam search
-    bl = BeamRun(wl.BEAM_LONG, dev)
-    bl.run(ctx, [], ev)
-    marks = []
-    for _ in range(reps):
-        bl.run(ctx, marks, ev)
-    torch.cuda.synchronize()
-    per = {}
-    for name, a, b in marks:
-        per.setdefault(name, []).append(a.elapsed_time(b) * 1e3)
+    bl = BeamRun(ctx, wl.BEAM_LONG, dev)
+    bl.run(ctx)
     res["beam_long_prompt"] = dict(
-        {"workload": "R8 x W400, P480, 5 steps, 24 layers, Hq14/Hkv2/D64, V151936"}, **bl.summary(per))
+        {"workload": "R8 x W400, P480, 5 steps, 24 layers, Hq14/Hkv2/D64, V151936"}, **time_beam(ctx, bl, ev, 20))
+    if full_cpu:
+        res["beam_long_prompt"]["cpu_oracle"] = oracle_beam_search_time(bl)
     del bl
     torch.cuda.empty_cache()
     # beam-search prompt prefill: R equal-length prompts packed, K/V kept in
@@ -355,81 +379,98 @@ def extra_workloads(ctx, dev, ev, reps=5):
 
 
 class BeamRun:
-    """Device-resident inputs of one fixed-step beam search and its launch
-    sequence: first merge (one beam in), then per step the all-layer decode
-    attention (history read through the last parents, suffix written in the
-    new order) and the merge, finally the suffix reorder by the last parents."""
+    """Device-resident inputs and preallocated state of one fixed-step beam
+    search.  run() is the product's one-call driver (slm_beam_search: first
+    merge with one beam in, then per step the all-layer decode attention and
+    the merge, finally the suffix reorder by the last parents and the
+    backtrack into token sequences); run_parts() issues the same launches one
+    by one with events between them, for the per-part breakdown."""
 
-    def __init__(self, bs, dev):
-        import torch
+    def __init__(self, ctx, bs, dev):
         import workloads as wl
         self.bs = bs
-        NL, R, W, P, N, V = bs.n_layers, bs.num_requests, bs.width, bs.prompt_len, bs.n_steps, bs.vocab
-        Hq, Hkv, D = bs.n_heads_q, bs.n_heads_kv, bs.head_dim
-        self.pk = wl.torch_normal_bf16((NL, R, P, Hkv, D), (bs.base_seed, wl.TID_PREFIX_K, 0, 0), dev)
-        self.pv = wl.torch_normal_bf16((NL, R, P, Hkv, D), (bs.base_seed, wl.TID_PREFIX_V, 0, 0), dev)
-        steps = range(1, N + 1)
-        self.q = [None] + [wl.torch_normal_bf16((NL, R, W, Hq, D), (bs.base_seed, wl.TID_Q, 0, t), dev) for t in steps]
-        self.kn = [None] + [wl.torch_normal_bf16((NL, R, W, Hkv, D), (bs.base_seed, wl.TID_K_NEW, 0, t), dev)
-                            for t in steps]
-        self.vn = [None] + [wl.torch_normal_bf16((NL, R, W, Hkv, D), (bs.base_seed, wl.TID_V_NEW, 0, t), dev)
-                            for t in steps]
-        self.lps = [wl.torch_logprobs((R, 1 if t == 0 else W, V), (bs.base_seed, wl.TID_LOGITS, 0, t), dev)
-                    for t in range(N + 1)]
-        self.cum0 = torch.zeros((R, 1), dtype=torch.float32, device=dev)
-        self.toks = [torch.empty((R, W), dtype=torch.int32, device=dev) for _ in range(N + 1)]
-        self.pars = [torch.empty((R, W), dtype=torch.int32, device=dev) for _ in range(N + 1)]
-        self.cums = [torch.empty((R, W), dtype=torch.float32, device=dev) for _ in range(N + 1)]
-        sshape = (NL, R, W, bs.suffix_cap, Hkv, D)
-        self.suf = [(torch.zeros(sshape, dtype=torch.bfloat16, device=dev),
-                     torch.zeros(sshape, dtype=torch.bfloat16, device=dev)) for _ in range(3)]
-        self.out = torch.empty((NL, R, W, Hq, D), dtype=torch.float32, device=dev)
+        self.x = wl.torch_beam_inputs(bs, dev)
+        self.st = ctx.beam_search_state(bs.n_layers, bs.num_requests, bs.width, bs.n_steps, bs.n_heads_q,
+                                        bs.n_heads_kv, bs.head_dim)
 
-    def run(self, ctx, marks, ev):
-        bs, N, W = self.bs, self.bs.n_steps, self.bs.width
+    def run(self, ctx):
+        x = self.x
+        ctx.beam_search(self.st, x["prefix_k"], x["prefix_v"], x["logprobs"], x["q"], x["k_new"], x["v_new"])
+
+    def run_parts(self, ctx, marks, ev):
+        x, st, N, W, R = self.x, self.st, self.bs.n_steps, self.bs.width, self.bs.num_requests
+        tok, par, cum = st["tokens"], st["parent"], st["cum"]
         e0 = ev()
-        ctx.beam_topk_merge(self.lps[0], self.cum0, W, self.toks[0], self.pars[0], self.cums[0])
+        ctx.beam_topk_merge(x["logprobs"][0], st["cum0"].view(R, 1), W, tok[0], par[0], cum[0])
         marks.append(("merge0", e0, ev()))
         for t in range(1, N + 1):
-            (ski, svi), (sko, svo) = self.suf[(t + 1) % 2], self.suf[t % 2]
+            ski, svi = (st["suffix_k"][(t + 1) % 2], st["suffix_v"][(t + 1) % 2]) if t > 1 else (None, None)
             e0 = ev()
-            ctx.beam_decode_attn(self.q[t], self.pk, self.pv, ski if t > 1 else None, svi if t > 1 else None,
-                                 self.kn[t], self.vn[t], self.pars[t - 1], t - 1, sko, svo, out=self.out)
+            ctx.beam_decode_attn(x["q"][t - 1], x["prefix_k"], x["prefix_v"], ski, svi, x["k_new"][t - 1],
+                                 x["v_new"][t - 1], par[t - 1], t - 1, st["suffix_k"][t % 2], st["suffix_v"][t % 2],
+                                 out=st["attn_out"][t - 1])
             e1 = ev()
-            ctx.beam_topk_merge(self.lps[t], self.cums[t - 1], W, self.toks[t], self.pars[t], self.cums[t])
+            ctx.beam_topk_merge(x["logprobs"][t], cum[t - 1], W, tok[t], par[t], cum[t])
             e2 = ev()
             marks.append(("decode%d" % t, e0, e1))
             marks.append(("merge%d" % t, e1, e2))
         e0 = ev()
-        ctx.beam_reorder_suffix(self.pars[N], self.suf[N % 2][0], self.suf[N % 2][1], N, self.suf[2][0],
-                                self.suf[2][1])
-        marks.append(("reorder", e0, ev()))
+        ctx.beam_reorder_suffix(par[N], st["suffix_k"][N % 2], st["suffix_v"][N % 2], N, st["final_k"], st["final_v"])
+        e1 = ev()
+        ctx.beam_backtrack(tok, par, out=st["sequences"])
+        marks.append(("reorder", e0, e1))
+        marks.append(("backtrack", e1, ev()))
 
-    def summary(self, per):
-        """Per-part averages (us) and the beam-step HBM fraction."""
+    def summary(self, per, search_us=None):
+        """Per-part medians (us) and the beam-step HBM fraction; search_us is
+        the one-call driver's time for the whole search, when measured."""
         bs = self.bs
         N, R, W, V = bs.n_steps, bs.num_requests, bs.width, bs.vocab
-        avg = {k: sum(v) / len(v) for k, v in per.items()}
+        med = {k: sorted(v)[len(v) // 2] for k, v in per.items()}
         parts = ["merge0"] + ["decode%d" % t for t in range(1, N + 1)] + ["merge%d" % t for t in range(1, N + 1)] \
-            + ["reorder"]
-        search_us = sum(avg[p] for p in parts)
-        step_us = [avg["decode%d" % t] + avg["merge%d" % t] for t in range(1, N + 1)]
+            + ["reorder", "backtrack"]
+        parts_us = sum(med[p] for p in parts)
+        search_us = parts_us if search_us is None else search_us
+        step_us = [med["decode%d" % t] + med["merge%d" % t] for t in range(1, N + 1)]
         step_bytes = [decode_bytes(bs, t) + topk_bytes(R, W, V, W) for t in range(1, N + 1)]
         return {
             "beam_search_us": round(search_us, 1),
+            "beam_search_parts_sum_us": round(parts_us, 1),
             "beam_step_us": [round(u, 1) for u in step_us],
             "beam_step_us_mean": round(sum(step_us) / N, 1),
             "beam_step_hbm_frac": [round(b / (u * 1e-6) / 1e9 / HBM_PEAK_GBS, 4) for b, u in zip(step_bytes, step_us)],
-            "decode_us": [round(avg["decode%d" % t], 1) for t in range(1, N + 1)],
-            "decode_hbm_frac": [round(decode_bytes(bs, t) / (avg["decode%d" % t] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+            "decode_us": [round(med["decode%d" % t], 1) for t in range(1, N + 1)],
+            "decode_hbm_frac": [round(decode_bytes(bs, t) / (med["decode%d" % t] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
                                 for t in range(1, N + 1)],
-            "merge_us": [round(avg["merge%d" % t], 1) for t in range(0, N + 1)],
-            "merge_hbm_frac": [round(topk_bytes(R, W, V, W) / (avg["merge%d" % t] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+            "merge_us": [round(med["merge%d" % t], 1) for t in range(0, N + 1)],
+            "merge_hbm_frac": [round(topk_bytes(R, W, V, W) / (med["merge%d" % t] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
                                for t in range(1, N + 1)],
-            "reorder_us": round(avg["reorder"], 1),
+            "reorder_us": round(med["reorder"], 1),
+            "backtrack_us": round(med["backtrack"], 1),
             "beam_requests_per_s": round(R / (search_us * 1e-6), 1),
-            "beams_steps_per_s": round(R * W * N / (sum(step_us) * 1e-6), 1),
+            "beams_steps_per_s": round(R * W * N / (search_us * 1e-6), 1),
+            "timing": "per-part medians of per-launch events over the repetitions; beam_search_us: median of the "
+                      "one-call driver",
         }
+
+
+def time_beam(ctx, run, ev, reps):
+    """Per-part medians from run_parts and the one-call driver's median time."""
+    import torch
+    marks, whole = [], []
+    for _ in range(reps):
+        run.run_parts(ctx, marks, ev)
+    for _ in range(reps):
+        e0 = ev()
+        run.run(ctx)
+        whole.append((e0, ev()))
+    torch.cuda.synchronize()
+    ctx.check()
+    per = {}
+    for name, a, b in marks:
+        per.setdefault(name, []).append(a.elapsed_time(b) * 1e3)
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in whole)[len(whole) // 2]
+    return run.summary(per, us)
 
 
 def main():
@@ -470,7 +511,7 @@ def main():
     pout = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
     gout = torch.empty((len(pf.lengths), pf.hidden_dim), dtype=torch.bfloat16, device=dev)
 
-    beam = BeamRun(bs, dev)
+    beam = BeamRun(ctx, bs, dev)
     torch.cuda.synchronize()
 
     def ev():
@@ -487,7 +528,9 @@ def main():
         e0 = ev()
         ctx.gather_last(hidden, cu, out=gout)
         marks.append(("gather", e0, ev()))
-        beam.run(ctx, marks, ev)
+        e0 = ev()
+        beam.run(ctx)
+        marks.append(("beam_search", e0, ev()))
 
     for _ in range(args.warmup):
         step([])
@@ -533,18 +576,23 @@ def main():
         torch.cuda.synchronize()
         ctx.check()
         graph_ms = g0.elapsed_time(g1) / args.steps
+        del g
 
     per = {}
     for name, a, b in marks:
         per.setdefault(name, []).append(a.elapsed_time(b) * 1e3)   # us
-    prefill_us = sum(per["prefill"]) / len(per["prefill"])
-    gather_us = sum(per["gather"]) / len(per["gather"])
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    prefill_us = sum(per["prefill"]) / len(per["prefill"])         # mean launch duration (roofline)
+    prefill_med = med(per["prefill"])
+    gather_us = med(per["gather"])
+    search_us = med(per["beam_search"])
+    beam_parts = time_beam(ctx, beam, ev, 20)                        # per-launch breakdown, outside the timed steps
 
     pbytes, pflops = prefill_bytes_flops(pf.lengths, Hq, Hkv, D, 4)
     achieved_gbs = pbytes / (prefill_us * 1e-6) / 1e9
     mfma_tflops = pflops / (prefill_us * 1e-6) / 1e12
     traffic = traffic_from_counters("prefill_attn.hip", "hbm_bytes_per_launch")
-    extra = {} if args.no_extra else extra_workloads(ctx, dev, ev)
+    extra = {} if args.no_extra else extra_workloads(ctx, dev, ev, full_cpu=args.cpu_baseline_full)
 
     value = pf.total_tokens / (ms_step * 1e-3)
     line = {
@@ -582,11 +630,13 @@ def main():
                                                        / MFMA_BF16_PEAK_TFLOPS), 4),
         },
         "parts": dict({
-            "prefill_layer_us": round(prefill_us, 2),
-            "prefill_28_layers_ms": round(prefill_us * pf.n_layers / 1e3, 3),
-            "prefill_tokens_per_s": round(pf.total_tokens / (prefill_us * pf.n_layers * 1e-6), 1),
+            "prefill_layer_us_median": round(prefill_med, 2),
+            "prefill_layer_us_mean": round(prefill_us, 2),
+            "prefill_28_layers_ms": round(prefill_med * pf.n_layers / 1e3, 3),
+            "prefill_tokens_per_s": round(pf.total_tokens / (prefill_med * pf.n_layers * 1e-6), 1),
             "gather_us": round(gather_us, 2),
-        }, **beam.summary(per), host_wall_s=round(t_wall, 3)),
+            "beam_search_one_call_us_in_step": round(search_us, 1),
+        }, **beam_parts, host_wall_s=round(t_wall, 3)),
     }
     if graph_ms is not None:
         line["graph_replay"] = {"ms_per_step": round(graph_ms, 4),
@@ -594,7 +644,7 @@ def main():
                                 "what": "the same step captured once as a HIP graph and replayed"}
     line.update(extra)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(pf, bs)
+        line["cpu_baseline"] = cpu_baseline(pf, (q, k, v, hidden), beam)
     print(json.dumps(line), flush=True)
 
 

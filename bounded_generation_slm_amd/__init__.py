@@ -38,7 +38,7 @@ EXPORTED = (
     "slm_abi_version", "slm_status_string", "slm_ctx_create", "slm_ctx_destroy",
     "slm_ctx_set_stream", "slm_ctx_check", "slm_ctx_last_error", "slm_packed_prefill_attn",
     "slm_gather_last", "slm_beam_decode_attn", "slm_beam_topk_merge", "slm_beam_topk_merge_logits",
-    "slm_beam_reorder_suffix", "slm_label_head", "slm_beam_backtrack",
+    "slm_beam_reorder_suffix", "slm_label_head", "slm_beam_backtrack", "slm_beam_search",
 )
 
 
@@ -56,6 +56,17 @@ class _BeamAttnArgs(ctypes.Structure):
             "q", "prefix_k", "prefix_v", "suffix_k_in", "suffix_v_in", "k_new", "v_new", "parent",
             "suffix_k_out", "suffix_v_out", "out")] + [("out_dtype", ctypes.c_int)] + [
         ("prompt_cu", ctypes.c_void_p), ("prompt_rows", ctypes.c_int32)]
+
+
+class _BeamSearchArgs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_layers", "num_requests", "width", "prompt_len", "n_steps", "suffix_cap", "n_heads_q", "n_heads_kv",
+        "head_dim", "vocab")] + [("scale", ctypes.c_float)] + [
+        (n, ctypes.c_void_p) for n in ("prefix_k", "prefix_v", "prompt_cu")] + [("prompt_rows", ctypes.c_int32)] + [
+        (n, ctypes.c_void_p) for n in ("cum0", "logprobs", "q", "k_new", "v_new")] + [
+        ("suffix_k", ctypes.c_void_p * 2), ("suffix_v", ctypes.c_void_p * 2)] + [
+        (n, ctypes.c_void_p) for n in ("final_k", "final_v", "attn_out")] + [("out_dtype", ctypes.c_int)] + [
+        (n, ctypes.c_void_p) for n in ("tokens", "parent", "cum", "sequences")]
 
 
 _P, _I, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
@@ -81,9 +92,10 @@ _lib.slm_beam_topk_merge_logits.argtypes = [_P, _P, ctypes.c_int, _P, _I, _I, _I
 _lib.slm_label_head.argtypes = [_P, _P, _P, _I, _I, _I, _P, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P]
 _lib.slm_beam_reorder_suffix.argtypes = [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
 _lib.slm_beam_backtrack.argtypes = [_P, _P, _P, _I, _I, _I, _P]
+_lib.slm_beam_search.argtypes = [_P, ctypes.POINTER(_BeamSearchArgs)]
 for _name in ("slm_ctx_create", "slm_ctx_set_stream", "slm_ctx_check", "slm_packed_prefill_attn",
               "slm_gather_last", "slm_beam_decode_attn", "slm_beam_topk_merge", "slm_beam_topk_merge_logits",
-              "slm_beam_reorder_suffix", "slm_label_head", "slm_beam_backtrack"):
+              "slm_beam_reorder_suffix", "slm_label_head", "slm_beam_backtrack", "slm_beam_search"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -190,6 +202,31 @@ class Context:
 
     def beam_backtrack(self, tokens, parent, out=None):
         return slm_beam_backtrack(self, tokens, parent, out)
+
+    def beam_search_state(self, n_layers: int, num_requests: int, width: int, n_steps: int, n_heads_q: int,
+                          n_heads_kv: int, head_dim: int, suffix_cap: Optional[int] = None,
+                          out_dtype=torch.float32, attn_per_step: bool = False) -> dict:
+        """Preallocated state of one fixed-step search (the load-time plan):
+        the two suffix buffers, the final suffix, the attention output (one
+        buffer, or one per step), the merge outputs and the sequences."""
+        NL, R, W, N = n_layers, num_requests, width, n_steps
+        S = N if suffix_cap is None else suffix_cap
+        dev = self.device
+        sshape = (NL, R, W, max(S, 1), n_heads_kv, head_dim)
+        z = lambda: torch.zeros(sshape, dtype=torch.bfloat16, device=dev)
+        one = torch.empty((NL, R, W, n_heads_q, head_dim), dtype=out_dtype, device=dev)
+        outs = [one] + [torch.empty_like(one) for _ in range(N - 1)] if attn_per_step else [one] * N
+        return dict(suffix_k=[z(), z()], suffix_v=[z(), z()], final_k=z(), final_v=z(), attn_out=outs,
+                    tokens=torch.empty((N + 1, R, W), dtype=torch.int32, device=dev),
+                    parent=torch.empty((N + 1, R, W), dtype=torch.int32, device=dev),
+                    cum=torch.empty((N + 1, R, W), dtype=torch.float32, device=dev),
+                    sequences=torch.empty((R, W, N + 1), dtype=torch.int32, device=dev),
+                    cum0=torch.zeros((R,), dtype=torch.float32, device=dev))
+
+    def beam_search(self, state: dict, prefix_k, prefix_v, logprobs, q, k_new, v_new, scale=None, prompt_cu=None,
+                    prompt_len: Optional[int] = None):
+        return slm_beam_search(self, state, prefix_k, prefix_v, logprobs, q, k_new, v_new, scale, prompt_cu,
+                               prompt_len)
 
     def label_head(self, hidden, cu_seqlens, lm_head, labels, k: int, label_map=None, probs: bool = True,
                    out=None):
@@ -422,3 +459,90 @@ def slm_beam_backtrack(ctx: Context, tokens, parent, out=None) -> torch.Tensor:
                                  _ptr(out, "out", (torch.int32,), dev))
     ctx._raise(rc, "slm_beam_backtrack")
     return out
+
+
+def slm_beam_search(ctx: Context, state: dict, prefix_k, prefix_v, logprobs, q, k_new, v_new, scale=None,
+                    prompt_cu=None, prompt_len: Optional[int] = None):
+    """The whole fixed-step search in one call.  logprobs: n_steps + 1 tensors ([R,1,V], then [R,W,V]);
+    q, k_new, v_new: n_steps tensors ([NL,R,W,Hq,D], [NL,R,W,Hkv,D]); prefix_k/v as for
+    slm_beam_decode_attn; state: from Context.beam_search_state (written in place).
+    Returns (tokens, parent, cum, sequences) of the state."""
+    dev = ctx.device
+    N = len(q)
+    if len(logprobs) != N + 1 or len(k_new) != N or len(v_new) != N or len(state["attn_out"]) != N:
+        raise ValueError("need n_steps + 1 log-prob tensors and n_steps q, k_new, v_new and attention outputs")
+    tokens, parent, cum, seq, cum0 = (state[k] for k in ("tokens", "parent", "cum", "sequences", "cum0"))
+    Np1, R, W = tokens.shape
+    if Np1 != N + 1 or tuple(parent.shape) != (Np1, R, W) or tuple(cum.shape) != (Np1, R, W):
+        raise ValueError("tokens, parent and cum must be [n_steps + 1, R, W]")
+    if seq is not None and tuple(seq.shape) != (R, W, Np1):
+        raise ValueError("sequences must be [R, W, n_steps + 1]")
+    if tuple(cum0.shape) != (R,):
+        raise ValueError("cum0 must be [R]")
+    V = logprobs[0].shape[-1]
+    for t, lp in enumerate(logprobs):
+        if tuple(lp.shape) != (R, 1 if t == 0 else W, V):
+            raise ValueError("logprobs[%d] must be [R, %s, V]" % (t, "1" if t == 0 else "W"))
+    D = prefix_k.shape[-1]
+    Hkv = prefix_k.shape[-2]
+    if N:
+        NL, _, _, Hq, _ = q[0].shape
+    else:
+        NL, Hq = prefix_k.shape[0], Hkv
+    if prompt_cu is None:
+        P = prefix_k.shape[2]
+        rows = R * P
+        if tuple(prefix_k.shape) != (NL, R, P, Hkv, D) or prefix_v.shape != prefix_k.shape:
+            raise ValueError("prefix_k/v must be [NL,R,P,Hkv,D]")
+    else:
+        if prompt_len is None:
+            raise ValueError("prompt_len (the longest prompt) is required with prompt_cu")
+        if tuple(prompt_cu.shape) != (R + 1,):
+            raise ValueError("prompt_cu must be [R+1]")
+        P, rows = int(prompt_len), prefix_k.shape[1]
+        if tuple(prefix_k.shape) != (NL, rows, Hkv, D) or prefix_v.shape != prefix_k.shape:
+            raise ValueError("packed prefix_k/v must be [NL,prompt_cu[R],Hkv,D]")
+    S_cap = state["final_k"].shape[3]
+    sshape = (NL, R, W, S_cap, Hkv, D)
+    for name in ("final_k", "final_v"):
+        if tuple(state[name].shape) != sshape:
+            raise ValueError("%s must be %s" % (name, sshape))
+    for name in ("suffix_k", "suffix_v"):
+        if len(state[name]) != 2 or any(tuple(t.shape) != sshape for t in state[name]):
+            raise ValueError("%s must be two %s buffers" % (name, sshape))
+    for t in range(N):
+        if tuple(q[t].shape) != (NL, R, W, Hq, D):
+            raise ValueError("q[%d] must be [NL,R,W,Hq,D]" % t)
+        if tuple(k_new[t].shape) != (NL, R, W, Hkv, D) or tuple(v_new[t].shape) != (NL, R, W, Hkv, D):
+            raise ValueError("k_new/v_new[%d] must be [NL,R,W,Hkv,D]" % t)
+        o = state["attn_out"][t]
+        if tuple(o.shape) != (NL, R, W, Hq, D) or o.dtype != state["attn_out"][0].dtype:
+            raise ValueError("attn_out[%d] must be [NL,R,W,Hq,D] of one dtype" % t)
+    out_dtype = state["attn_out"][0].dtype if N else torch.float32
+    if out_dtype not in _OUT:
+        raise ValueError("attention output must be float32 or bfloat16")
+    arr = lambda ts, name, dt: (ctypes.c_void_p * max(1, len(ts)))(*[_ptr(t, name, dt, dev) for t in ts])
+    lp_a = arr(logprobs, "logprobs", (torch.float32,))
+    q_a, kn_a, vn_a = arr(q, "q", _BF16), arr(k_new, "k_new", _BF16), arr(v_new, "v_new", _BF16)
+    o_a = arr(state["attn_out"], "attn_out", tuple(_OUT))
+    a = _BeamSearchArgs()
+    a.n_layers, a.num_requests, a.width, a.prompt_len, a.n_steps, a.suffix_cap = NL, R, W, P, N, S_cap
+    a.n_heads_q, a.n_heads_kv, a.head_dim, a.vocab = Hq, Hkv, D, V
+    a.scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    a.prefix_k, a.prefix_v = _ptr(prefix_k, "prefix_k", _BF16, dev), _ptr(prefix_v, "prefix_v", _BF16, dev)
+    a.prompt_cu = _ptr(prompt_cu, "prompt_cu", (torch.int32,), dev)
+    a.prompt_rows = rows
+    a.cum0 = _ptr(cum0, "cum0", (torch.float32,), dev)
+    a.logprobs, a.q, a.k_new, a.v_new, a.attn_out = (ctypes.cast(x, ctypes.c_void_p) for x in (lp_a, q_a, kn_a,
+                                                                                               vn_a, o_a))
+    for i in range(2):
+        a.suffix_k[i] = _ptr(state["suffix_k"][i], "suffix_k", _BF16, dev)
+        a.suffix_v[i] = _ptr(state["suffix_v"][i], "suffix_v", _BF16, dev)
+    a.final_k, a.final_v = _ptr(state["final_k"], "final_k", _BF16, dev), _ptr(state["final_v"], "final_v", _BF16, dev)
+    a.out_dtype = _OUT[out_dtype]
+    a.tokens, a.parent = _ptr(tokens, "tokens", (torch.int32,), dev), _ptr(parent, "parent", (torch.int32,), dev)
+    a.cum = _ptr(cum, "cum", (torch.float32,), dev)
+    a.sequences = _ptr(seq, "sequences", (torch.int32,), dev)
+    ctx._stream()
+    ctx._raise(_lib.slm_beam_search(ctx._h, ctypes.byref(a)), "slm_beam_search")
+    return tokens, parent, cum, seq

@@ -20,7 +20,6 @@
 // current beam order (parent's history rows + the new row), so the reorder
 // after the previous merge costs no separate pass.
 #include <map>
-#include <mutex>
 #include <type_traits>
 
 #include "attn_tile.h"
@@ -471,7 +470,7 @@ int decode_chunks(int64_t units, int blocks32, int waves, int64_t resident) {
 }
 
 template <int D, bool OUT_BF16, int NTHR, bool STAGE>
-hipError_t launch_variant(const DecodeParams& p, int num_cus, hipStream_t stream) {
+hipError_t launch_variant(const DecodeParams& p, int num_cus, LaunchCache& cache, hipStream_t stream) {
     const int n_units = p.n_layers * p.num_requests * p.n_heads_kv;
     const int M = p.width * p.group;
     const int blocks32 = (M + 31) / 32;
@@ -481,28 +480,23 @@ hipError_t launch_variant(const DecodeParams& p, int num_cus, hipStream_t stream
     auto kern = beam_decode_attn_kernel<D, OUT_BF16, NTHR, STAGE>;
     // raise the kernel's dynamic-LDS limit only when a call needs more than
     // before, and query the workgroups per CU once per LDS size (no host call
-    // per launch, so launches can be graph-captured); the lock keeps the
-    // recorded values and the attribute in step across threads
-    static std::mutex lds_mu;
-    static size_t lds_limit = 0;
-    static std::map<size_t, int> occ;            // workgroups per CU by LDS size
-    int per_cu;
-    {
-        std::lock_guard<std::mutex> lock(lds_mu);
-        if (lds > lds_limit) {
-            hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            if (e != hipSuccess) return e;
-            lds_limit = lds;
-        }
-        auto it = occ.find(lds);
-        if (it == occ.end()) {
-            int n = 0;
-            hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)kern, NTHR, lds);
-            if (e != hipSuccess) return e;
-            it = occ.emplace(lds, max(1, n)).first;
-        }
-        per_cu = it->second;
+    // per launch, so launches can be graph-captured); the context's cache
+    // records both for its device
+    const int variant = (D == 128) * 8 + OUT_BF16 * 4 + (NTHR == 1024) * 2 + STAGE;
+    size_t& lds_limit = cache.decode_lds_limit[variant];
+    if (lds > lds_limit) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        lds_limit = lds;
     }
+    auto it = cache.decode_occ.find({variant, lds});
+    if (it == cache.decode_occ.end()) {
+        int n = 0;
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)kern, NTHR, lds);
+        if (e != hipSuccess) return e;
+        it = cache.decode_occ.emplace(std::make_pair(variant, lds), max(1, n)).first;
+    }
+    const int per_cu = it->second;
     int chunks = decode_chunks(units_padded, blocks32, NTHR / kWave, (int64_t)num_cus * per_cu);
     const int chunk_rows = (blocks32 + chunks - 1) / chunks * 32;
     chunks = (M + chunk_rows - 1) / chunk_rows;
@@ -518,7 +512,7 @@ size_t beam_decode_lds_bytes(int head_dim, int prompt_len) {
 }
 
 hipError_t launch_beam_decode_attn(const DecodeParams& p, int head_dim, bool out_bf16, int num_cus,
-                                   hipStream_t stream) {
+                                   LaunchCache& cache, hipStream_t stream) {
     // A prompt copy too large for two workgroups per CU is shared by 16 waves
     // (head_dim 64; at 128 the registers of 16 waves would not hold a lane's state).
     // The fp32 output is staged through LDS where the tiles still leave room
@@ -527,14 +521,14 @@ hipError_t launch_beam_decode_attn(const DecodeParams& p, int head_dim, bool out
     const bool wide = head_dim == 64 && prompt_lds > kDecSmallLds;
     const bool stage = head_dim == 64 && !out_bf16 && prompt_lds + 8 * kStageWaveBytes <= kDecSmallLds;
     if (head_dim == 128)
-        return out_bf16 ? launch_variant<128, true, 512, false>(p, num_cus, stream)
-                        : launch_variant<128, false, 512, false>(p, num_cus, stream);
+        return out_bf16 ? launch_variant<128, true, 512, false>(p, num_cus, cache, stream)
+                        : launch_variant<128, false, 512, false>(p, num_cus, cache, stream);
     if (out_bf16)
-        return wide ? launch_variant<64, true, 1024, false>(p, num_cus, stream)
-                    : launch_variant<64, true, 512, false>(p, num_cus, stream);
-    if (stage) return launch_variant<64, false, 512, true>(p, num_cus, stream);
-    return wide ? launch_variant<64, false, 1024, false>(p, num_cus, stream)
-                : launch_variant<64, false, 512, false>(p, num_cus, stream);
+        return wide ? launch_variant<64, true, 1024, false>(p, num_cus, cache, stream)
+                    : launch_variant<64, true, 512, false>(p, num_cus, cache, stream);
+    if (stage) return launch_variant<64, false, 512, true>(p, num_cus, cache, stream);
+    return wide ? launch_variant<64, false, 1024, false>(p, num_cus, cache, stream)
+                : launch_variant<64, false, 512, false>(p, num_cus, cache, stream);
 }
 
 }  // namespace slm

@@ -4,7 +4,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <utility>
+
 namespace slm {
+
+// Per-context launch state: the resident workgroups per CU of each kernel
+// variant and the dynamic-LDS limits already raised, recorded the first time
+// a variant or LDS size is seen, so later launches make no host query (and
+// can be captured into a graph).  A context lives on one device, so nothing
+// here is shared across devices.
+struct LaunchCache {
+    int prefill_per_cu[2][2][2] = {};                   // [head_dim 128][two heads per block][bf16 out]
+    std::map<std::pair<int, size_t>, int> decode_occ;   // (variant, LDS bytes) -> workgroups per CU
+    std::map<int, size_t> decode_lds_limit;             // variant -> dynamic-LDS limit already set
+};
 
 // Device error codes written to the context's flag word.
 enum DeviceError : int {
@@ -38,7 +52,7 @@ struct PrefillParams {
     int plan_cap;                       // capacity of plan_items
 };
 hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, bool out_bf16, bool persistent,
-                               int num_cus, hipStream_t stream);
+                               int num_cus, LaunchCache& cache, hipStream_t stream);
 // the persistent form stages cu_seqlens in LDS: packs of fewer sequences only
 constexpr int kPrefillPlanMaxSeqs = 15999;
 // plan entries a pack can need: sum over sequences of ceil(L / qt_rows), per unit column
@@ -117,7 +131,7 @@ struct DecodeParams {
     int prompt_rows;            // rows per layer of the packed prompts (prompt_cu[R])
 };
 hipError_t launch_beam_decode_attn(const DecodeParams& p, int head_dim, bool out_bf16, int num_cus,
-                                   hipStream_t stream);
+                                   LaunchCache& cache, hipStream_t stream);
 
 struct TopkParams {
     const float* logprobs;

@@ -662,8 +662,8 @@ hipError_t launch_variant(const PrefillParams& p, hipStream_t stream) {
 }
 
 template <int D, int NH, bool OUT_BF16>
-hipError_t launch_persistent(const PrefillParams& p, int num_cus, hipStream_t stream) {
-    static int per_cu = 0;                      // resident workgroups per CU (one device type)
+hipError_t launch_persistent(const PrefillParams& p, int num_cus, LaunchCache& cache, hipStream_t stream) {
+    int& per_cu = cache.prefill_per_cu[D == 128][NH == 2][OUT_BF16];   // resident workgroups per CU
     if (per_cu == 0) {
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &per_cu, (const void*)prefill_persistent_kernel<D, NH, OUT_BF16>, 256, 0);
@@ -679,28 +679,28 @@ hipError_t launch_persistent(const PrefillParams& p, int num_cus, hipStream_t st
 }
 
 template <int D, int NH, bool OUT_BF16>
-hipError_t dispatch(const PrefillParams& p, bool persistent, int num_cus, hipStream_t stream) {
-    return persistent ? launch_persistent<D, NH, OUT_BF16>(p, num_cus, stream)
+hipError_t dispatch(const PrefillParams& p, bool persistent, int num_cus, LaunchCache& cache, hipStream_t stream) {
+    return persistent ? launch_persistent<D, NH, OUT_BF16>(p, num_cus, cache, stream)
                       : launch_variant<D, NH, OUT_BF16>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, bool out_bf16, bool persistent, int num_cus,
-                               hipStream_t stream) {
+                               LaunchCache& cache, hipStream_t stream) {
     const int nh = p.heads_per_block;
     if (head_dim == 128) {
         if (nh == 2)
-            return out_bf16 ? dispatch<128, 2, true>(p, persistent, num_cus, stream)
-                            : dispatch<128, 2, false>(p, persistent, num_cus, stream);
-        return out_bf16 ? dispatch<128, 1, true>(p, persistent, num_cus, stream)
-                        : dispatch<128, 1, false>(p, persistent, num_cus, stream);
+            return out_bf16 ? dispatch<128, 2, true>(p, persistent, num_cus, cache, stream)
+                            : dispatch<128, 2, false>(p, persistent, num_cus, cache, stream);
+        return out_bf16 ? dispatch<128, 1, true>(p, persistent, num_cus, cache, stream)
+                        : dispatch<128, 1, false>(p, persistent, num_cus, cache, stream);
     }
     if (nh == 2)
-        return out_bf16 ? dispatch<64, 2, true>(p, persistent, num_cus, stream)
-                        : dispatch<64, 2, false>(p, persistent, num_cus, stream);
-    return out_bf16 ? dispatch<64, 1, true>(p, persistent, num_cus, stream)
-                    : dispatch<64, 1, false>(p, persistent, num_cus, stream);
+        return out_bf16 ? dispatch<64, 2, true>(p, persistent, num_cus, cache, stream)
+                        : dispatch<64, 2, false>(p, persistent, num_cus, cache, stream);
+    return out_bf16 ? dispatch<64, 1, true>(p, persistent, num_cus, cache, stream)
+                    : dispatch<64, 1, false>(p, persistent, num_cus, cache, stream);
 }
 
 }  // namespace slm

@@ -22,6 +22,7 @@
 struct slm_ctx {
     int device = 0;
     bool dry_run = false;   // device < 0: validate arguments only, touch no device
+    bool validating = false;   // slm_beam_search's first pass: validate every launch, issue none
     hipStream_t stream = nullptr;
     slm_caps caps{};
     uint64_t* topk_ws = nullptr;    // [R] 512-byte state lines (threshold, count, slots), then [R] key lists
@@ -34,6 +35,7 @@ struct slm_ctx {
     size_t max_lds = 0;
     int topk_blocks_per_cu[slm::kTopkMaxWidth + 1] = {0};   // stage-1 occupancy per width (0 = not queried)
     int topk_logits_blocks_per_cu[slm::kTopkMaxWidth + 1] = {0};   // the same, merge on logits
+    slm::LaunchCache launch_cache;  // occupancy and LDS limits of the attention kernels on this device
     char last_error[512] = {0};
 };
 
@@ -54,9 +56,10 @@ slm_status ok(slm_ctx* ctx) {
     return SLM_OK;
 }
 
-// Validation passed: a dry-run context stops here, others launch.
+// Validation passed: a dry-run context (or a validation pass) stops here,
+// others launch.
 #define SLM_LAUNCH(ctx, call, what) \
-    ((ctx)->dry_run ? ok(ctx) : launched((ctx), (call), (what)))
+    (((ctx)->dry_run || (ctx)->validating) ? ok(ctx) : launched((ctx), (call), (what)))
 
 slm_status launched(slm_ctx* ctx, hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(ctx, SLM_ERR_DEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
@@ -268,7 +271,7 @@ slm_status slm_packed_prefill_attn(slm_ctx* ctx, const uint16_t* q, const uint16
     const int64_t est_units = ((int64_t)total_tokens * n_heads_q / 128) + 1;
     const bool persistent = est_units >= 8LL * ctx->num_cus && num_seqs <= slm::kPrefillPlanMaxSeqs;
     return SLM_LAUNCH(ctx, slm::launch_prefill_attn(p, head_dim, out_dtype == SLM_BF16, persistent, ctx->num_cus,
-                                                    ctx->stream), "prefill");
+                                                    ctx->launch_cache, ctx->stream), "prefill");
 }
 
 slm_status slm_gather_last(slm_ctx* ctx, const void* hidden, const int32_t* cu_seqlens, int32_t num_seqs,
@@ -401,7 +404,7 @@ slm_status slm_beam_decode_attn(slm_ctx* ctx, const slm_beam_attn_args* a) {
     p.prompt_cu = a->prompt_cu;
     p.prompt_rows = (int)prompt_rows;
     return SLM_LAUNCH(ctx, slm::launch_beam_decode_attn(p, a->head_dim, a->out_dtype == SLM_BF16, ctx->num_cus,
-                                                                ctx->stream),
+                                                        ctx->launch_cache, ctx->stream),
                       "decode");
 }
 
@@ -444,8 +447,12 @@ slm_status slm_beam_topk_merge(slm_ctx* ctx, const float* logprobs, const float*
     p.num_requests = num_requests; p.beams_in = beams_in; p.vocab = vocab; p.width = width;
     // stage-1 waves take equal ranges of the flattened candidates, one per
     // resident wave (four waves per workgroup)
-    int& bpc = ctx->topk_blocks_per_cu[width];
-    if (bpc == 0) bpc = ctx->dry_run ? 1 : slm::beam_topk_blocks_per_cu(width);
+    int bpc = ctx->topk_blocks_per_cu[width];
+    if (bpc == 0) {
+        const bool query = !ctx->dry_run && !ctx->validating;
+        bpc = query ? slm::beam_topk_blocks_per_cu(width) : 1;
+        if (query) ctx->topk_blocks_per_cu[width] = bpc;
+    }
     const int64_t resident = (int64_t)ctx->num_cus * bpc * 4;
     p.seg = slm::beam_topk_segment(num_requests, beams_in, vocab, resident, ctx->topk_lists);
     return SLM_LAUNCH(ctx, slm::launch_beam_topk_merge(p, ctx->stream), "topk");
@@ -506,8 +513,12 @@ slm_status slm_beam_topk_merge_logits(slm_ctx* ctx, const void* logits, slm_dtyp
     p.level2_w = ctx->caps.max_beams;
     p.level2_cnt = (int*)(p.level2 + R_cap * slm::kTopkLogitChunks * p.level2_w);
     p.num_requests = num_requests; p.beams_in = beams_in; p.vocab = vocab; p.width = width;
-    int& bpc = ctx->topk_logits_blocks_per_cu[width];
-    if (bpc == 0) bpc = ctx->dry_run ? 1 : slm::beam_topk_logits_blocks_per_cu(width);
+    int bpc = ctx->topk_logits_blocks_per_cu[width];
+    if (bpc == 0) {
+        const bool query = !ctx->dry_run && !ctx->validating;
+        bpc = query ? slm::beam_topk_logits_blocks_per_cu(width) : 1;
+        if (query) ctx->topk_logits_blocks_per_cu[width] = bpc;
+    }
     const int64_t resident = (int64_t)ctx->num_cus * bpc * 4;
     p.seg = slm::beam_topk_logits_segment(num_requests, beams_in, vocab, resident, ctx->topk_lists, parts_cap, p.rpw,
                                           p.rows_per_chunk, p.chunks);
@@ -565,6 +576,90 @@ slm_status slm_beam_backtrack(slm_ctx* ctx, const int32_t* tokens, const int32_t
     p.tokens = tokens; p.parent = parent; p.seq = sequences; p.err = ctx->err_flag;
     p.n_merges = n_merges; p.num_requests = num_requests; p.width = width;
     return SLM_LAUNCH(ctx, slm::launch_backtrack(p, ctx->stream), "backtrack");
+}
+
+namespace {
+
+// The launches of one fixed-step beam search, in order (see slm_beam_search).
+// Stops at the first status other than SLM_OK.
+slm_status beam_search_launches(slm_ctx* ctx, const slm_beam_search_args* a) {
+    const int N = a->n_steps, R = a->num_requests, W = a->width;
+    const size_t rw = (size_t)R * W;
+    slm_status s = slm_beam_topk_merge(ctx, a->logprobs[0], a->cum0, R, 1, a->vocab, W, a->tokens, a->parent,
+                                       a->cum);
+    if (s != SLM_OK) return s;
+    for (int t = 1; t <= N; ++t) {
+        slm_beam_attn_args d{};
+        d.n_layers = a->n_layers; d.num_requests = R; d.width = W; d.prompt_len = a->prompt_len;
+        d.hist_len = t - 1; d.suffix_cap = a->suffix_cap; d.n_heads_q = a->n_heads_q; d.n_heads_kv = a->n_heads_kv;
+        d.head_dim = a->head_dim; d.scale = a->scale;
+        d.q = a->q[t - 1]; d.prefix_k = a->prefix_k; d.prefix_v = a->prefix_v;
+        d.suffix_k_in = t > 1 ? a->suffix_k[(t + 1) % 2] : nullptr;
+        d.suffix_v_in = t > 1 ? a->suffix_v[(t + 1) % 2] : nullptr;
+        d.k_new = a->k_new[t - 1]; d.v_new = a->v_new[t - 1];
+        d.parent = a->parent + (t - 1) * rw;
+        d.suffix_k_out = a->suffix_k[t % 2]; d.suffix_v_out = a->suffix_v[t % 2];
+        d.out = a->attn_out[t - 1]; d.out_dtype = a->out_dtype;
+        d.prompt_cu = a->prompt_cu; d.prompt_rows = a->prompt_rows;
+        s = slm_beam_decode_attn(ctx, &d);
+        if (s != SLM_OK) return s;
+        s = slm_beam_topk_merge(ctx, a->logprobs[t], a->cum + (t - 1) * rw, R, W, a->vocab, W, a->tokens + t * rw,
+                                a->parent + t * rw, a->cum + t * rw);
+        if (s != SLM_OK) return s;
+    }
+    if (N > 0) {
+        s = slm_beam_reorder_suffix(ctx, a->n_layers, R, W, N, a->suffix_cap, a->n_heads_kv, a->head_dim,
+                                    a->parent + N * rw, a->suffix_k[N % 2], a->suffix_v[N % 2], a->final_k,
+                                    a->final_v);
+        if (s != SLM_OK) return s;
+    }
+    if (a->sequences) s = slm_beam_backtrack(ctx, a->tokens, a->parent, N + 1, R, W, a->sequences);
+    return s;
+}
+
+}  // namespace
+
+slm_status slm_beam_search(slm_ctx* ctx, const slm_beam_search_args* a) {
+    slm_status s = enter(ctx);
+    if (s != SLM_OK) return s;
+    if (!a) return fail(ctx, SLM_ERR_INVALID_ARG, "beam_search: NULL args");
+    if (a->n_steps < 0 || a->n_steps > slm::kDecodeMaxSuffix || a->num_requests <= 0 || a->width <= 0 ||
+        a->vocab <= 0)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "beam_search: n_steps %d outside [0, %d] or a size out of range",
+                    a->n_steps, slm::kDecodeMaxSuffix);
+    if (!a->logprobs || !a->cum0 || !a->tokens || !a->parent || !a->cum)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "beam_search: NULL pointer");
+    if (a->n_steps > 0 && (!a->q || !a->k_new || !a->v_new || !a->attn_out || !a->final_k || !a->final_v))
+        return fail(ctx, SLM_ERR_INVALID_ARG, "beam_search: NULL per-step pointer array or final suffix");
+    if (a->n_steps > 0 && a->suffix_cap < a->n_steps)
+        return fail(ctx, SLM_ERR_INVALID_ARG, "beam_search: suffix_cap %d < n_steps %d", a->suffix_cap, a->n_steps);
+    const size_t rw = (size_t)a->num_requests * a->width, nb = ((size_t)a->n_steps + 1) * rw * 4;
+    if (overlaps(a->tokens, nb, a->parent, nb) || overlaps(a->tokens, nb, a->cum, nb) ||
+        overlaps(a->parent, nb, a->cum, nb))
+        return fail(ctx, SLM_ERR_ALIAS, "beam_search: tokens, parent and cum overlap");
+    if (a->n_steps > 0) {
+        const size_t sb = (size_t)a->n_layers * rw * a->suffix_cap * a->n_heads_kv * a->head_dim * 2;
+        const void* bufs[] = {a->suffix_k[0], a->suffix_k[1], a->suffix_v[0], a->suffix_v[1], a->final_k, a->final_v};
+        for (int i = 0; i < 6; ++i) {
+            if (!bufs[i]) return fail(ctx, SLM_ERR_INVALID_ARG, "beam_search: NULL suffix buffer");
+            for (int j = 0; j < i; ++j)
+                if (overlaps(bufs[i], sb, bufs[j], sb))
+                    return fail(ctx, SLM_ERR_ALIAS, "beam_search: suffix buffers overlap each other");
+        }
+        const size_t ob = (size_t)a->n_layers * rw * a->n_heads_q * a->head_dim * (a->out_dtype == SLM_F32 ? 4 : 2);
+        const void* state[] = {a->tokens, a->parent, a->cum};
+        for (int t = 0; t < a->n_steps; ++t)
+            for (const void* p : state)
+                if (overlaps(a->attn_out[t], ob, p, nb))
+                    return fail(ctx, SLM_ERR_ALIAS, "beam_search: attention output %d overlaps the merge state", t);
+    }
+    // every launch's own validation first, so that an invalid argument
+    // anywhere in the sequence leaves nothing launched
+    ctx->validating = true;
+    s = beam_search_launches(ctx, a);
+    ctx->validating = false;
+    if (s != SLM_OK || ctx->dry_run) return s;
+    return beam_search_launches(ctx, a);
 }
 
 }  // extern "C"

@@ -40,7 +40,8 @@
 extern "C" {
 #endif
 
-#define SLM_ABI_VERSION 4   /* 3: slm_beam_attn_args gained prompt_cu, prompt_rows; 4: slm_beam_backtrack */
+#define SLM_ABI_VERSION 4   /* 3: slm_beam_attn_args gained prompt_cu, prompt_rows;
+                               4: slm_beam_backtrack, slm_beam_search */
 
 typedef enum {
     SLM_OK = 0,
@@ -275,6 +276,55 @@ slm_status slm_beam_reorder_suffix(slm_ctx *ctx, int32_t n_layers, int32_t num_r
  */
 slm_status slm_beam_backtrack(slm_ctx *ctx, const int32_t *tokens, const int32_t *parent, int32_t n_merges,
                               int32_t num_requests, int32_t width, int32_t *sequences);
+
+/*
+ * The whole fixed-step beam search of R requests in one call (§1.1: a
+ * beam-search request runs a fixed number of decode steps at a fixed width;
+ * abstract and §02: the fixed Beam Search is compiled into one node, with no
+ * per-step control from the host).  The call enqueues, on the context's
+ * stream and with no host synchronisation:
+ *   merge 0   slm_beam_topk_merge(logprobs[0] [R,1,V], cum0 [R,1], W)
+ *             -> tokens[0], parent[0], cum[0]
+ *   for t = 1 .. n_steps:
+ *     decode  slm_beam_decode_attn: hist_len = t-1, q[t-1], k_new[t-1],
+ *             v_new[t-1], parents parent[t-1], suffix read from
+ *             suffix_k/v[(t+1) % 2] (not at t = 1) and written to
+ *             suffix_k/v[t % 2], attention into attn_out[t-1]
+ *     merge t slm_beam_topk_merge(logprobs[t] [R,W,V], cum[t-1], W)
+ *             -> tokens[t], parent[t], cum[t]
+ *   reorder   slm_beam_reorder_suffix(parent[n_steps], rows n_steps) from
+ *             suffix_k/v[n_steps % 2] into final_k/final_v (n_steps > 0)
+ *   backtrack slm_beam_backtrack(tokens, parent) -> sequences (if not NULL)
+ * Every launch's arguments are validated before the first is issued, so an
+ * error leaves nothing enqueued.  The host pointer arrays (logprobs, q,
+ * k_new, v_new, attn_out) are read during the call only; the call can be
+ * captured into a graph.  Shapes and rules are those of the calls above;
+ * tokens, parent and cum are [n_steps + 1, R, W], sequences [R, W,
+ * n_steps + 1]; n_steps <= 8 and suffix_cap >= n_steps; the suffix and final
+ * buffers must not overlap each other, nor attn_out the merge state.
+ * attn_out entries may repeat (one buffer overwritten every step).
+ */
+typedef struct {
+    int32_t n_layers, num_requests, width, prompt_len, n_steps, suffix_cap;
+    int32_t n_heads_q, n_heads_kv, head_dim, vocab;
+    float scale;
+    const uint16_t *prefix_k, *prefix_v;   /* [NL, R, P, Hkv, D], or packed with prompt_cu */
+    const int32_t *prompt_cu;              /* [R+1] or NULL, as in slm_beam_attn_args */
+    int32_t prompt_rows;
+    const float *cum0;                     /* [R] initial scores (zeros for fresh requests) */
+    const float *const *logprobs;          /* n_steps + 1 device pointers: [R,1,V], then [R,W,V] */
+    const uint16_t *const *q;              /* n_steps device pointers [NL, R, W, Hq, D] */
+    const uint16_t *const *k_new;          /* n_steps device pointers [NL, R, W, Hkv, D] */
+    const uint16_t *const *v_new;          /* n_steps device pointers [NL, R, W, Hkv, D] */
+    uint16_t *suffix_k[2], *suffix_v[2];   /* [NL, R, W, S_cap, Hkv, D] each, used alternately */
+    uint16_t *final_k, *final_v;           /* [NL, R, W, S_cap, Hkv, D]: rows < n_steps in the last order */
+    void *const *attn_out;                 /* n_steps device pointers [NL, R, W, Hq, D] */
+    slm_dtype out_dtype;
+    int32_t *tokens, *parent;              /* [n_steps + 1, R, W] */
+    float *cum;                            /* [n_steps + 1, R, W] */
+    int32_t *sequences;                    /* [R, W, n_steps + 1] or NULL */
+} slm_beam_search_args;
+slm_status slm_beam_search(slm_ctx *ctx, const slm_beam_search_args *args);
 
 #ifdef __cplusplus
 }

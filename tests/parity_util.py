@@ -38,3 +38,24 @@ def assert_attn_close(got: np.ndarray, ref: np.ndarray, what: str = ""):
     assert rel <= REL_L2 and mab <= MAX_ABS, "%s: rel_l2 %.3g (<= %g), max_abs %.3g (<= %g)" % (
         what, rel, REL_L2, mab, MAX_ABS)
     return rel, mab
+
+
+def assert_attn_close_chunked(got, ref: np.ndarray, what: str = "", rows: int = 8192):
+    """assert_attn_close over a whole (large) tensor, a block of leading rows
+    at a time: got is a device tensor, ref the fp64 oracle array."""
+    assert tuple(got.shape) == ref.shape, (tuple(got.shape), ref.shape)
+    num = den = 0.0
+    mab = 0.0
+    for i in range(0, ref.shape[0], rows):
+        g = got[i:i + rows].float().cpu().numpy().astype(np.float64)
+        r = ref[i:i + rows]
+        assert np.all(np.isfinite(g)), what + ": non-finite output"
+        d = g - r
+        num += float(np.sum(d * d))
+        den += float(np.sum(r * r))
+        if d.size:
+            mab = max(mab, float(np.abs(d).max()))
+    rel = (num ** 0.5) / max(den ** 0.5, 1e-30)
+    assert rel <= REL_L2 and mab <= MAX_ABS, "%s: rel_l2 %.3g (<= %g), max_abs %.3g (<= %g)" % (
+        what, rel, REL_L2, mab, MAX_ABS)
+    return rel, mab

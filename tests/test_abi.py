@@ -245,3 +245,34 @@ def test_backtrack_validation(dry):
     assert _status(lambda: dry.beam_backtrack(buf[:24].view(3, 2, 4), par, out=buf[12:36].view(2, 4, 3))) \
         == slm.SLM_ERR_ALIAS
     assert _status(lambda: dry.beam_backtrack(tok[:0], par[:0])) == slm.SLM_ERR_INVALID_ARG   # no merge
+
+
+def _search(dry, NL=2, R=2, W=3, P=5, N=3, Hq=4, Hkv=2, D=64, V=50):
+    st = dry.beam_search_state(NL, R, W, N, Hq, Hkv, D)
+    pk, pv = _bf(NL, R, P, Hkv, D), _bf(NL, R, P, Hkv, D)
+    lps = [torch.zeros((R, 1 if t == 0 else W, V)) for t in range(N + 1)]
+    q = [_bf(NL, R, W, Hq, D) for _ in range(N)]
+    kn = [_bf(NL, R, W, Hkv, D) for _ in range(N)]
+    return st, pk, pv, lps, q, kn, [t.clone() for t in kn]
+
+
+def test_beam_search_validation(dry):
+    """The fixed-step driver validates every launch of its sequence before it
+    issues any; state of the wrong shape is refused by the binding."""
+    st, pk, pv, lps, q, kn, vn = _search(dry)
+    assert _status(lambda: dry.beam_search(st, pk, pv, lps, q, kn, vn)) == slm.SLM_OK
+    bad = dict(st)
+    bad["final_k"] = st["suffix_k"][0]                              # final buffer aliases a suffix buffer
+    assert _status(lambda: dry.beam_search(bad, pk, pv, lps, q, kn, vn)) == slm.SLM_ERR_ALIAS
+    with pytest.raises(ValueError):
+        dry.beam_search(st, pk, pv, lps[:-1], q, kn, vn)                # one log-prob tensor short
+    big = _search(dry, V=50, W=3)
+    lp_wide = [torch.zeros((2, 1, 2))] + [torch.zeros((2, 3, 2))] * 3   # W = 3 > Win * V at the first merge
+    assert _status(lambda: dry.beam_search(big[0], big[1], big[2], lp_wide, big[4], big[5], big[6])) \
+        == slm.SLM_ERR_INVALID_ARG
+    st9 = dry.beam_search_state(1, 1, 2, 9, 4, 2, 64)
+    lp9 = [torch.zeros((1, 1, 10))] + [torch.zeros((1, 2, 10))] * 9
+    q9 = [_bf(1, 1, 2, 4, 64)] * 9
+    k9 = [_bf(1, 1, 2, 2, 64)] * 9
+    assert _status(lambda: dry.beam_search(st9, _bf(1, 1, 3, 2, 64), _bf(1, 1, 3, 2, 64), lp9, q9, k9, k9)) \
+        == slm.SLM_ERR_INVALID_ARG                                   # more than 8 steps

@@ -284,3 +284,52 @@ def test_beam_sequence_tiny(gpu):
         assert np.array_equal(got["suffix_v"][t][:, :, :, :t + 1], ref["suffix_v"][t][:, :, :, :t + 1])
     assert np.array_equal(got["final_suffix_k"], ref["final_suffix_k"])
     assert np.array_equal(got["final_suffix_v"], ref["final_suffix_v"])
+
+
+def test_beam_search_driver_tiny(gpu):
+    """The one-call driver on the tiny beam shape: every output against the
+    oracle's fixed-step sequence (merges bit-exact, attention of each step
+    within tolerance, final suffix and backtracked sequences bit-exact)."""
+    note("beam search driver tiny_beam, 4 steps")
+    shape = wl.TINY_BEAM
+    N = shape.n_steps
+    st = wl.beam_static_inputs(shape)
+    steps = {t: wl.beam_step_inputs(shape, t) for t in range(1, N + 1)}
+    lps = [wl.beam_logprobs(shape, t) for t in range(N + 1)]
+    state = gpu.beam_search_state(shape.n_layers, shape.num_requests, shape.width, N, shape.n_heads_q,
+                                  shape.n_heads_kv, shape.head_dim, attn_per_step=True)
+    gpu.beam_search(state, dev_bf16(st["prefix_k"]), dev_bf16(st["prefix_v"]),
+                    [torch.from_numpy(lp).cuda() for lp in lps], [dev_bf16(steps[t]["q"]) for t in steps],
+                    [dev_bf16(steps[t]["k_new"]) for t in steps], [dev_bf16(steps[t]["v_new"]) for t in steps])
+    gpu.check()
+    ref = oracle.beam_search(steps.__getitem__, st["prefix_k"], st["prefix_v"], lps.__getitem__, shape.width, N)
+    for t in range(N + 1):
+        _eq((state["tokens"][t].cpu().numpy(), state["parent"][t].cpu().numpy(), state["cum"][t].cpu().numpy()),
+            (ref["tokens"][t], ref["parent"][t], ref["cum"][t]), "merge %d" % t)
+    for t in range(N):
+        assert_attn_close(host_f64(state["attn_out"][t]), ref["attn"][t], "attn step %d" % (t + 1))
+    assert np.array_equal(host_bits(state["final_k"]), ref["final_suffix_k"])
+    assert np.array_equal(host_bits(state["final_v"]), ref["final_suffix_v"])
+    assert np.array_equal(state["sequences"].cpu().numpy(), ref["sequences"])
+
+
+@pytest.mark.parametrize("n,R,W", [(1, 3, 5), (5, 2, 100), (6, 8, 400)])
+def test_backtrack(gpu, n, R, W):
+    note("backtrack n=%d R=%d W=%d" % (n, R, W))
+    rng = np.random.default_rng(n * 100 + W)
+    tok = rng.integers(0, 151936, size=(n, R, W)).astype(np.int32)
+    par = rng.integers(0, W, size=(n, R, W)).astype(np.int32)
+    par[0] = 0
+    seq = gpu.beam_backtrack(torch.from_numpy(tok).cuda(), torch.from_numpy(par).cuda())
+    gpu.check()
+    assert np.array_equal(seq.cpu().numpy(), oracle.beam_backtrack(tok, par))
+
+
+def test_backtrack_bad_parent_is_flagged(gpu):
+    note("backtrack bad parent -> device error flag")
+    tok = torch.zeros((3, 1, 4), dtype=torch.int32, device="cuda")
+    par = torch.zeros((3, 1, 4), dtype=torch.int32, device="cuda")
+    par[2, 0, 1] = 9
+    gpu.beam_backtrack(tok, par)
+    with pytest.raises(Exception, match="parent"):
+        gpu.check()

@@ -238,6 +238,23 @@ def torch_logprobs(shape, seed_tuple, device):
     return out
 
 
+def torch_beam_inputs(shape: BeamShape, device) -> dict:
+    """Device-drawn inputs of one fixed-step search of ``shape``: prompt K/V
+    ``[NL,R,P,Hkv,D]``, per decode step t = 1..N the q ``[NL,R,W,Hq,D]`` and
+    k_new/v_new ``[NL,R,W,Hkv,D]`` (lists indexed t-1), and the log-probs of
+    the N+1 merges (``[R,1,V]``, then ``[R,W,V]``)."""
+    NL, R, W, P, N, V = shape.n_layers, shape.num_requests, shape.width, shape.prompt_len, shape.n_steps, shape.vocab
+    Hq, Hkv, D, b = shape.n_heads_q, shape.n_heads_kv, shape.head_dim, shape.base_seed
+    steps = range(1, N + 1)
+    return dict(
+        prefix_k=torch_normal_bf16((NL, R, P, Hkv, D), (b, TID_PREFIX_K, 0, 0), device),
+        prefix_v=torch_normal_bf16((NL, R, P, Hkv, D), (b, TID_PREFIX_V, 0, 0), device),
+        q=[torch_normal_bf16((NL, R, W, Hq, D), (b, TID_Q, 0, t), device) for t in steps],
+        k_new=[torch_normal_bf16((NL, R, W, Hkv, D), (b, TID_K_NEW, 0, t), device) for t in steps],
+        v_new=[torch_normal_bf16((NL, R, W, Hkv, D), (b, TID_V_NEW, 0, t), device) for t in steps],
+        logprobs=[torch_logprobs((R, 1 if t == 0 else W, V), (b, TID_LOGITS, 0, t), device) for t in range(N + 1)])
+
+
 def _fold_seed(seed_tuple) -> int:
     """Fold a seed tuple into one 63-bit torch seed (SplitMix64 steps)."""
     h = 0x9E3779B97F4A7C15
