@@ -39,6 +39,7 @@ EXPORTED = (
     "slm_ctx_set_stream", "slm_ctx_check", "slm_ctx_last_error", "slm_packed_prefill_attn",
     "slm_gather_last", "slm_beam_decode_attn", "slm_beam_topk_merge", "slm_beam_topk_merge_logits",
     "slm_beam_reorder_suffix", "slm_label_head", "slm_beam_backtrack", "slm_beam_search",
+    "slm_packed_prefill_attn_noalloc",
 )
 
 
@@ -71,7 +72,7 @@ class _BeamSearchArgs(ctypes.Structure):
 
 _P, _I, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
 _lib.slm_abi_version.restype = ctypes.c_int
-_ABI = 4                                  # the struct layouts above and the symbol set
+_ABI = 5                                  # the struct layouts above and the symbol set
 if _lib.slm_abi_version() != _ABI:
     raise ImportError("%s has ABI version %d, this binding expects %d: rebuild it with "
                       "bounded_generation_slm_amd/_build.py" % (LIB_PATH, _lib.slm_abi_version(), _ABI))
@@ -93,9 +94,11 @@ _lib.slm_label_head.argtypes = [_P, _P, _P, _I, _I, _I, _P, _I, _P, _I, _I, _P, 
 _lib.slm_beam_reorder_suffix.argtypes = [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
 _lib.slm_beam_backtrack.argtypes = [_P, _P, _P, _I, _I, _I, _P]
 _lib.slm_beam_search.argtypes = [_P, ctypes.POINTER(_BeamSearchArgs)]
+_lib.slm_packed_prefill_attn_noalloc.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, ctypes.c_int, _P]
 for _name in ("slm_ctx_create", "slm_ctx_set_stream", "slm_ctx_check", "slm_packed_prefill_attn",
               "slm_gather_last", "slm_beam_decode_attn", "slm_beam_topk_merge", "slm_beam_topk_merge_logits",
-              "slm_beam_reorder_suffix", "slm_label_head", "slm_beam_backtrack", "slm_beam_search"):
+              "slm_beam_reorder_suffix", "slm_label_head", "slm_beam_backtrack", "slm_beam_search",
+              "slm_packed_prefill_attn_noalloc"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -546,3 +549,37 @@ def slm_beam_search(ctx: Context, state: dict, prefix_k, prefix_v, logprobs, q, 
     ctx._stream()
     ctx._raise(_lib.slm_beam_search(ctx._h, ctypes.byref(a)), "slm_beam_search")
     return tokens, parent, cum, seq
+
+
+def slm_packed_prefill_attn_noalloc(q, k, v, cu_seqlens, max_seqlen: int, scale: Optional[float] = None,
+                                    out: Optional[torch.Tensor] = None, out_dtype=torch.float32,
+                                    err_flag: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """slm_packed_prefill_attn without a context and without any allocation in
+    the library (its scratch memory is a static array of the device): on q's
+    device and torch's current stream.  Pass ``out`` to allocate nothing at
+    all; ``err_flag`` (one int32 on the device, zeroed by the caller) receives
+    a nonzero code when cu_seqlens breaks the caller guarantees."""
+    if not isinstance(q, torch.Tensor) or q.device.type != "cuda":
+        raise ValueError("q must be a device tensor")
+    dev = q.device
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (T, Hkv, D) or v.shape != (T, Hkv, D):
+        raise ValueError("k and v must be [T, Hkv, D] matching q")
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=out_dtype, device=dev)
+    if out.shape != (T, Hq, D) or out.dtype not in _OUT:
+        raise ValueError("out must be [T, Hq, D] float32 or bfloat16")
+    if err_flag is not None and (err_flag.numel() != 1 or err_flag.dtype != torch.int32):
+        raise ValueError("err_flag must be one int32")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = _lib.slm_packed_prefill_attn_noalloc(
+            _P(stream), _ptr(q, "q", _BF16, dev), _ptr(k, "k", _BF16, dev), _ptr(v, "v", _BF16, dev),
+            _ptr(cu_seqlens, "cu_seqlens", (torch.int32,), dev), cu_seqlens.numel() - 1, T, int(max_seqlen), Hq, Hkv,
+            D, scale, _ptr(out, "out", tuple(_OUT), dev), _OUT[out.dtype], _ptr(err_flag, "err_flag", (torch.int32,), dev))
+    if rc != SLM_OK:
+        raise SlmError(rc, "slm_packed_prefill_attn_noalloc (a pack's work list holds T*Hq/128 + B*Hq <= 262144 "
+                           "entries)")
+    return out

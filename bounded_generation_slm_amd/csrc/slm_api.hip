@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/slm.h"
@@ -122,6 +123,8 @@ slm_status slm_ctx_create(int device, const slm_caps* caps, slm_ctx** out) {
         if (c.max_heads_q <= 0) c.max_heads_q = 64;
         ctx->caps = c;
         ctx->max_lds = 160 * 1024;          // gfx950 LDS per workgroup
+        ctx->plan_cap = (int)std::min<int64_t>(slm::prefill_plan_entries(c.max_tokens, c.max_seqs, c.max_heads_q),
+                                               INT32_MAX - 16);
         *out = ctx;
         return SLM_OK;
     }
@@ -242,6 +245,9 @@ slm_status slm_packed_prefill_attn(slm_ctx* ctx, const uint16_t* q, const uint16
     if (total_tokens > ctx->caps.max_tokens || num_seqs > ctx->caps.max_seqs || n_heads_q > ctx->caps.max_heads_q)
         return fail(ctx, SLM_ERR_CAPACITY, "prefill: beyond the context caps (tokens %d, seqs %d, heads %d)",
                     ctx->caps.max_tokens, ctx->caps.max_seqs, ctx->caps.max_heads_q);
+    if (slm::prefill_plan_entries(total_tokens, num_seqs, n_heads_q) > ctx->plan_cap)
+        return fail(ctx, SLM_ERR_CAPACITY, "prefill: the pack's work list (%lld entries) exceeds the workspace (%d)",
+                    (long long)slm::prefill_plan_entries(total_tokens, num_seqs, n_heads_q), ctx->plan_cap);
     const size_t T = (size_t)total_tokens, D = (size_t)head_dim;
     const size_t qb = T * n_heads_q * D * 2, kb = T * n_heads_kv * D * 2;
     const size_t ob = T * n_heads_q * D * (out_dtype == SLM_F32 ? 4 : 2);
@@ -663,3 +669,71 @@ slm_status slm_beam_search(slm_ctx* ctx, const slm_beam_search_args* a) {
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Packed prefill without any allocation, for callers that cannot allocate
+// device memory.  The persistent form's work list, its per-XCD counters and a
+// device error word live in `scratch`, a fixed array of every device the
+// library runs on; its address on a device is looked up once, with that
+// device current, the first time the call runs there.
+namespace {
+
+constexpr int kNoAllocPlanEntries = 1 << 18;        // work-list entries (16 bytes each): 4 MiB
+constexpr int kNoAllocDevices = 64;
+// [kNoAllocPlanEntries] work list, [8] per-XCD counts / offsets / claims
+// (written by the plan kernel of every call), [1] the error word used when the
+// caller passes no flag of its own
+static __device__ __align__(256) int4 scratch[kNoAllocPlanEntries + 9];
+
+struct NoAllocDevice {
+    std::mutex mu;            // host-side state of the device (not the device array)
+    bool ready = false;
+    slm_ctx ctx;              // no workspace of its own: plan_items is this device's scratch
+};
+NoAllocDevice g_noalloc[kNoAllocDevices];
+
+slm_status noalloc_setup(NoAllocDevice& nd, int dev) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SLM_ERR_DEVICE;
+    int cus = 0, lds = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+        return SLM_ERR_DEVICE;
+    slm_ctx& c = nd.ctx;
+    c.device = dev;
+    c.num_cus = cus;
+    c.max_lds = (size_t)lds;
+    c.caps = slm_caps{1, 1, 1, INT32_MAX, INT32_MAX, INT32_MAX};   // bounded by the work list below
+    c.plan_items = (int4*)ptr;
+    c.plan_cap = kNoAllocPlanEntries;
+    c.err_flag = (int*)((int4*)ptr + kNoAllocPlanEntries + 8);
+    nd.ready = true;
+    return SLM_OK;
+}
+
+}  // namespace
+
+extern "C" slm_status slm_packed_prefill_attn_noalloc(void* hip_stream, const uint16_t* q, const uint16_t* k,
+                                                      const uint16_t* v, const int32_t* cu_seqlens, int32_t num_seqs,
+                                                      int32_t total_tokens, int32_t max_seqlen, int32_t n_heads_q,
+                                                      int32_t n_heads_kv, int32_t head_dim, float scale, void* out,
+                                                      slm_dtype out_dtype, int32_t* err_flag) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SLM_ERR_DEVICE;
+    if (dev < 0 || dev >= kNoAllocDevices) return SLM_ERR_UNSUPPORTED;
+    NoAllocDevice& nd = g_noalloc[dev];
+    std::lock_guard<std::mutex> lock(nd.mu);
+    if (!nd.ready) {
+        const slm_status s = noalloc_setup(nd, dev);
+        if (s != SLM_OK) return s;
+    }
+    slm_ctx& c = nd.ctx;
+    int* const own_flag = c.err_flag;
+    c.stream = (hipStream_t)hip_stream;
+    if (err_flag) c.err_flag = err_flag;
+    const slm_status s = slm_packed_prefill_attn(&c, q, k, v, cu_seqlens, num_seqs, total_tokens, max_seqlen,
+                                                 n_heads_q, n_heads_kv, head_dim, scale, out, out_dtype);
+    c.err_flag = own_flag;
+    c.stream = nullptr;
+    return s;
+}

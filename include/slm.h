@@ -40,8 +40,9 @@
 extern "C" {
 #endif
 
-#define SLM_ABI_VERSION 4   /* 3: slm_beam_attn_args gained prompt_cu, prompt_rows;
-                               4: slm_beam_backtrack, slm_beam_search */
+#define SLM_ABI_VERSION 5   /* 3: slm_beam_attn_args gained prompt_cu, prompt_rows;
+                               4: slm_beam_backtrack, slm_beam_search;
+                               5: slm_packed_prefill_attn_noalloc */
 
 typedef enum {
     SLM_OK = 0,
@@ -325,6 +326,37 @@ typedef struct {
     int32_t *sequences;                    /* [R, W, n_steps + 1] or NULL */
 } slm_beam_search_args;
 slm_status slm_beam_search(slm_ctx *ctx, const slm_beam_search_args *args);
+
+/*
+ * Packed prefill that allocates nothing, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  It needs no context: it runs on the calling
+ * thread's current device, on `hip_stream` (a hipStream_t of that device;
+ * NULL = null stream), and computes exactly what slm_packed_prefill_attn
+ * computes, with the same arguments, rules and statuses, through the same
+ * kernels.
+ *   - Its scratch memory (the persistent form's work list, its per-XCD
+ *     counters and an error word) is one static array per device, 4 MiB +
+ *     144 bytes, held until the process ends.  The work list bounds the pack:
+ *     total_tokens * n_heads_q / 128 + num_seqs * n_heads_q must be at most
+ *     262,144 (e.g. 1M tokens at 16 query heads with up to 8,192 sequences),
+ *     else SLM_ERR_CAPACITY and nothing is launched.
+ *   - Every call on a device shares that device's array, which keeps the
+ *     last call's contents (each call rewrites what it reads).  Calls that
+ *     overlap on one device -- on two streams, or from two processes' views
+ *     of the same array -- race; serialise them.
+ *   - err_flag: a device int32 the kernels set to a nonzero code when
+ *     cu_seqlens breaks the caller guarantees (the caller zeroes it and reads
+ *     it; the library never clears it); NULL: not reported.
+ *   - No detail string: slm_ctx_last_error does not cover this call.
+ * The first call on a device looks up the array's address there
+ * (hipGetSymbolAddress); no call allocates or frees memory.
+ */
+slm_status slm_packed_prefill_attn_noalloc(void *hip_stream, const uint16_t *q, const uint16_t *k,
+                                           const uint16_t *v, const int32_t *cu_seqlens, int32_t num_seqs,
+                                           int32_t total_tokens, int32_t max_seqlen, int32_t n_heads_q,
+                                           int32_t n_heads_kv, int32_t head_dim, float scale, void *out,
+                                           slm_dtype out_dtype, int32_t *err_flag);
 
 #ifdef __cplusplus
 }

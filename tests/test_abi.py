@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert declared == set(slm.EXPORTED)
-    assert slm.abi_version() == 4
+    assert slm.abi_version() == 5
 
 
 @pytest.fixture
