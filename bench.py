@@ -58,6 +58,9 @@ def parse():
                     help="skip the reporting-only prefill-request and long-prompt beam timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--kernels-only", action="store_true",
+                    help="untimed: two launches of every hot-path workload (960-sequence prefill layer, gather, "
+                         "short- and long-prompt searches), for counter collection, then exit")
     return ap.parse_args()
 
 
@@ -513,6 +516,18 @@ def main():
 
     beam = BeamRun(ctx, bs, dev)
     torch.cuda.synchronize()
+
+    if args.kernels_only:
+        long_run = BeamRun(ctx, wl.BEAM_LONG, dev)
+        for _ in range(2):
+            ctx.packed_prefill_attn(q, k, v, cu, pf.max_seqlen, out=pout)
+            ctx.gather_last(hidden, cu, out=gout)
+            beam.run(ctx)
+            long_run.run(ctx)
+        torch.cuda.synchronize()
+        ctx.check()
+        print(json.dumps({"kernels_only": "2 x (prefill layer, gather, short-prompt search, long-prompt search)"}))
+        return
 
     def ev():
         e = torch.cuda.Event(enable_timing=True)

@@ -29,6 +29,12 @@
 namespace slm {
 namespace {
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// c + a.lo * b.lo + a.hi * b.hi over packed bf16 pairs, fp32 accumulation (v_dot2c_f32_bf16)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
 constexpr size_t kDecSmallLds = 80 * 1024;     // two workgroups per CU fit
 // fp32 output staged per wave through LDS, one 32-column half of the 32-row
 // block at a time (row pitch 36 floats: the 16-byte writes of 16 lanes and
@@ -299,104 +305,44 @@ __global__ __launch_bounds__(NTHR, (D == 64 ? 4 : 2)) void beam_decode_attn_kern
         // ---- the beam's own suffix: parent's history rows, then the new row ----
         if (src < 0 || src >= W) src = w;         // flagged by the suffix copy above
         const int ns = p.hist_len + 1;
-        if constexpr (NTHR == 512) {
-            // One row at a time with the online update; a row's K and V halves
-            // are loaded together, so each row costs one memory round trip.
+        // One row at a time with the online update; a row's K and V halves
+        // are loaded together, so each row costs one memory round trip,
+        // and the dot products take the bf16 pairs as they are (v_dot2).
 #pragma unroll 1
-            for (int i = 0; i < ns; ++i) {
-                const bool hist = i < p.hist_len;
-                const int64_t ro = hist ? ((((int64_t)lr * W + src) * p.suffix_cap + i) * Hkv + g) * D
-                                        : (((int64_t)lr * W + w) * Hkv + g) * D;
-                const uint16_t* kr = (hist ? p.suffix_k_in : p.k_new) + ro;
-                const uint16_t* vr = (hist ? p.suffix_v_in : p.v_new) + ro;
-                u32x4 kv[NKS];
-                u32x2 vv[NDB * 4];
+        for (int i = 0; i < ns; ++i) {
+            const bool hist = i < p.hist_len;
+            const int64_t ro = hist ? ((((int64_t)lr * W + src) * p.suffix_cap + i) * Hkv + g) * D
+                                    : (((int64_t)lr * W + w) * Hkv + g) * D;
+            const uint16_t* kr = (hist ? p.suffix_k_in : p.k_new) + ro;
+            const uint16_t* vr = (hist ? p.suffix_v_in : p.v_new) + ro;
+            u32x4 kv[NKS];
+            u32x2 vv[NDB * 4];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) kv[ks] = *(const u32x4*)(kr + ks * 16 + hf * 8);
+            for (int ks = 0; ks < NKS; ++ks) kv[ks] = *(const u32x4*)(kr + ks * 16 + hf * 8);
 #pragma unroll
-                for (int j = 0; j < NDB * 4; ++j) vv[j] = *(const u32x2*)(vr + (j >> 2) * 32 + 8 * (j & 3) + 4 * hf);
-                float part = 0.f;
+            for (int j = 0; j < NDB * 4; ++j) vv[j] = *(const u32x2*)(vr + (j >> 2) * 32 + 8 * (j & 3) + 4 * hf);
+            float part = 0.f;
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
+            for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        part += bf16_bits_to_f32(qreg[ks][e] & 0xFFFFu) * bf16_bits_to_f32(kv[ks][e] & 0xFFFFu);
-                        part += bf16_bits_to_f32(qreg[ks][e] >> 16) * bf16_bits_to_f32(kv[ks][e] >> 16);
-                    }
-                part += __shfl_xor(part, 32);
-                const float s = part * p.scale_log2;
-                const float mnew = fmaxf(mrun, s);     // finite: s is
-                const float alpha = fast_exp2(mrun - mnew);
-                const float pi = fast_exp2(s - mnew);
-                mrun = mnew;
-                lsum = lsum * alpha + (hf == 0 ? pi : 0.f);   // both halves hold the same score
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int i4 = 0; i4 < 4; ++i4) {
-                        const u32x2 x = vv[db * 4 + i4];
-                        o[db][4 * i4 + 0] = o[db][4 * i4 + 0] * alpha + pi * bf16_bits_to_f32(x[0] & 0xFFFFu);
-                        o[db][4 * i4 + 1] = o[db][4 * i4 + 1] * alpha + pi * bf16_bits_to_f32(x[0] >> 16);
-                        o[db][4 * i4 + 2] = o[db][4 * i4 + 2] * alpha + pi * bf16_bits_to_f32(x[1] & 0xFFFFu);
-                        o[db][4 * i4 + 3] = o[db][4 * i4 + 3] * alpha + pi * bf16_bits_to_f32(x[1] >> 16);
-                    }
-            }
-        } else {
-            // The 16-wave workgroup (long prompts) is bound by its prompt pass;
-            // there all scores first, then one rescale and the V rows measured
-            // faster than the row loop.
-            float sc[8];                              // host guarantees hist_len + 1 <= 8
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                sc[i] = -INFINITY;
-                if (i < ns) {
-                    const uint16_t* kr = i < p.hist_len
-                        ? p.suffix_k_in + ((((int64_t)lr * W + src) * p.suffix_cap + i) * Hkv + g) * D
-                        : p.k_new + (((int64_t)lr * W + w) * Hkv + g) * D;
-                    float part = 0.f;
-#pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) {
-                        const u32x4 kv = *(const u32x4*)(kr + ks * 16 + hf * 8);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            part += bf16_bits_to_f32(qreg[ks][e] & 0xFFFFu) * bf16_bits_to_f32(kv[e] & 0xFFFFu);
-                            part += bf16_bits_to_f32(qreg[ks][e] >> 16) * bf16_bits_to_f32(kv[e] >> 16);
-                        }
-                    }
-                    part += __shfl_xor(part, 32);
-                    sc[i] = part * p.scale_log2;
-                }
-            }
-            float smax = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) smax = fmaxf(smax, sc[i]);
-            const float mnew = fmaxf(mrun, smax);     // finite: the new row is always there
+                for (int e = 0; e < 4; ++e) part = dot2_bf16(qreg[ks][e], kv[ks][e], part);
+            part += __shfl_xor(part, 32);
+            const float s = part * p.scale_log2;
+            const float mnew = fmaxf(mrun, s);     // finite: s is
             const float alpha = fast_exp2(mrun - mnew);
-            lsum *= alpha;
+            const float pi = fast_exp2(s - mnew);
+            mrun = mnew;
+            lsum = lsum * alpha + (hf == 0 ? pi : 0.f);   // both halves hold the same score
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (i < ns) {
-                    const float pi = fast_exp2(sc[i] - mnew);
-                    if (hf == 0) lsum += pi;          // both halves hold the same score
-                    const uint16_t* vr = i < p.hist_len
-                        ? p.suffix_v_in + ((((int64_t)lr * W + src) * p.suffix_cap + i) * Hkv + g) * D
-                        : p.v_new + (((int64_t)lr * W + w) * Hkv + g) * D;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                        for (int i4 = 0; i4 < 4; ++i4) {
-                            const u32x2 vv = *(const u32x2*)(vr + db * 32 + 8 * i4 + 4 * hf);
-                            o[db][4 * i4 + 0] += pi * bf16_bits_to_f32(vv[0] & 0xFFFFu);
-                            o[db][4 * i4 + 1] += pi * bf16_bits_to_f32(vv[0] >> 16);
-                            o[db][4 * i4 + 2] += pi * bf16_bits_to_f32(vv[1] & 0xFFFFu);
-                            o[db][4 * i4 + 3] += pi * bf16_bits_to_f32(vv[1] >> 16);
-                        }
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const u32x2 x = vv[db * 4 + i4];
+                    o[db][4 * i4 + 0] = o[db][4 * i4 + 0] * alpha + pi * bf16_bits_to_f32(x[0] & 0xFFFFu);
+                    o[db][4 * i4 + 1] = o[db][4 * i4 + 1] * alpha + pi * bf16_bits_to_f32(x[0] >> 16);
+                    o[db][4 * i4 + 2] = o[db][4 * i4 + 2] * alpha + pi * bf16_bits_to_f32(x[1] & 0xFFFFu);
+                    o[db][4 * i4 + 3] = o[db][4 * i4 + 3] * alpha + pi * bf16_bits_to_f32(x[1] >> 16);
                 }
-            }
         }
 
         lsum += __shfl_xor(lsum, 32);
