@@ -300,19 +300,22 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const Prefil
 // run side by side and its K/V is read from HBM about once and from the XCD's
 // L2 after that.
 //
-// Vector-memory instructions are counted so that each tile's wait covers that
-// tile and nothing newer: per tile 2*LPW direct loads, at the end of an item
-// NST unconditional buffer stores and NKS Q loads for the next item (inline
-// asm).  Wave 0 also issues one counter atomic per item; it is left out of
-// the counts, which can only make a wait cover one more operation.
+// A step covers 64 keys: two 32-key tiles, staged together in one half of a
+// four-tile LDS ring while the next step's two tiles load into the other
+// half, so each workgroup barrier, wait and issue serves 64 keys.
+//
+// Vector-memory instructions are counted so that each step's wait covers its
+// two tiles and nothing newer: per step 4*LPW direct loads, then, at the end
+// of an item, NST unconditional buffer stores and NKS Q loads for the next
+// item (inline asm).  Wave 0 also issues one counter atomic per item; it is
+// left out of the counts, which can only make a wait cover one more operation.
 //
 // A ticket reaches the other waves through LDS.  The ticket for the next item
-// is claimed when two tiles of the current one are left to load, just before
-// a tile's loads; two steps later the wait for that tile has covered it, and
-// wave 0 writes it to LDS before that step's barrier.  The issue side reads it
-// when it starts the next item, which is exactly then.  Only items of a single
-// tile need it sooner: wave 0 then waits for all its memory operations and the
-// workgroup takes one extra barrier.
+// is claimed with the loads of an item's first step, just before them; the
+// next step's wait has covered it, and wave 0 writes it to LDS before that
+// step's barrier.  The issue side needs it one step later at the earliest
+// (an item of a single step), so it has always been published; a defensive
+// path still waits for it explicitly should it not have been.
 // One counter increment by lane `sel` (0 or 1) of the wave; the old value
 // lands in that lane of tk, written in place (tk is an in/out operand, so the
 // register is never copied while the atomic is in flight).
@@ -371,9 +374,14 @@ struct PersistentTask {
     using E = Epi<D, OUT_BF16>;
     static constexpr int QT = 128 / NH;
     static constexpr int WPH = 4 / NH;
-    static constexpr int DMA = 2 * G::LPW;      // vector-memory ops per tile issue
+    static constexpr int KS = 2 * kKT;          // keys per step
+    static constexpr int DMA = 4 * G::LPW;      // vector-memory ops per step's tile issue
     static constexpr int QL = G::NKS;           // Q loads per item
     static constexpr int ST = E::NST;           // output stores per item
+    // the epilogue stages its rows in the half of the ring the finished step
+    // read (after a barrier), where it fits; else in an area of its own
+    static constexpr bool EPI_IN_RING = 4 * E::WAVEB <= 2 * G::STAGEB;
+    static constexpr int LDS_BYTES = 4 * G::STAGEB + (EPI_IN_RING ? 0 : 4 * E::WAVEB);
 
     // fixed
     const PrefillParams* pp;
@@ -383,16 +391,16 @@ struct PersistentTask {
     int cnt, wx, lane, wave, n, hf;
     float c;
     int64_t kv_stride, out_bytes;
-    uint32_t wbuf, slot_addr;
+    uint32_t ring_addr, slot_addr;
     LaneConst<D> lc;
     // ticket of the next item (lane 0 of wave 0) and the LDS slot it is published in
     uint32_t tk;
     int slot_item, slot_pub;                    // item the slot holds, step whose barrier published it
     bool pend;                                  // a claimed ticket is not yet published
     int pend_item, pend_ps;                     // its item and the step from which it has landed
-    // issue side: two tiles ahead of the compute side
+    // issue side: one step ahead of the compute side
     PItem iu;
-    int ki, ti;                                 // item number and next tile within it
+    int ki, ti;                                 // item number and next step within it
     bool claimed;                               // the ticket of item ki + 1 is claimed
     bool need_next;                             // iu is fully issued: start item ki + 1 at the next call
     bool idone;                                 // no item after iu
@@ -404,7 +412,7 @@ struct PersistentTask {
     u32x4 qreg[G::NKS];
     f32x16 o[G::NDB];
     float m, lsum;
-    int end1, end2;                             // what the two previous steps issued at their end: 0 nothing,
+    int end1;                                   // what the previous step issued at its end: 0 nothing,
                                                 // 1 a store burst (ST ops), 2 stores then Q loads (ST + QL ops)
     bool fresh, done;
     int step_no;
@@ -417,7 +425,7 @@ struct PersistentTask {
         u.g = e.z / pp->head_blocks;
         u.h0 = u.g * pp->group + (e.z % pp->head_blocks) * NH;
         u.q0 = e.w * QT;
-        u.ntiles = (min(u.q0 + QT, u.L) + kKT - 1) / kKT;
+        u.ntiles = (min(u.q0 + QT, u.L) + KS - 1) / KS;     // steps of 64 keys
         return u;
     }
 
@@ -428,13 +436,14 @@ struct PersistentTask {
         pend = false;
     }
 
-    template <int STAGE>
+    // The two tiles of the issue side's next step into ring half HALF.
+    template <int HALF>
     __device__ __forceinline__ void issue_next(int step) {
         if (need_next) {                        // start item ki + 1
             need_next = false;
             const int want = ki + 1;
             const bool ready = opaque_uniform(slot_item) == want && opaque_uniform(slot_pub) <= step;
-            if (!ready) {                       // single-tile item: wait for the ticket explicitly
+            if (!ready) {                       // not expected: wait for the ticket explicitly
                 if (wave == 0) wait_vmcnt<0>();
                 if (pend) publish(step);
                 __builtin_amdgcn_s_barrier();
@@ -452,17 +461,18 @@ struct PersistentTask {
                 idone = true;
             }
         }
-        if (!idone && !claimed && iu.ntiles - ti <= 2) {   // ticket of item ki + 1, before this call's loads
+        if (!idone && !claimed) {               // ticket of item ki + 1, before this item's first loads
             if (wave == 0) claim_ticket(tk, 0, counter);
             claimed = true;
             pend = true;
             pend_item = ki + 1;
-            pend_ps = step + 2;
+            pend_ps = step + 1;
         }
         const uint16_t* kb = pp->k + (int64_t)iu.s0 * kv_stride + (int64_t)iu.g * D;
         const uint16_t* vb = pp->v + (int64_t)iu.s0 * kv_stride + (int64_t)iu.g * D;
-        const int t = idone ? iu.ntiles - 1 : ti;   // past the last item: re-read its last tile
-        issue_tile<D, STAGE>(ring, lc, kb, vb, kv_stride, t * kKT, iu.L, wave);
+        const int t = idone ? iu.ntiles - 1 : ti;   // past the last item: re-read its last step's tiles
+        issue_tile<D, 2 * HALF>(ring, lc, kb, vb, kv_stride, t * KS, iu.L, wave);
+        issue_tile<D, 2 * HALF + 1>(ring, lc, kb, vb, kv_stride, t * KS + kKT, iu.L, wave);
         if (!idone && ++ti == iu.ntiles) need_next = true;
     }
 
@@ -487,9 +497,10 @@ struct PersistentTask {
     }
 
     // The finished item's output: rows u.s0 + u.q0 .. +QT of heads u.h0 ..
-    // +NH, stored with buffer stores (offsets of rows outside the sequence are
-    // out of range, so those stores are dropped and the count is fixed).
-    __device__ __forceinline__ void epilogue(const PItem& u, int u_wrow0, int u_h) {
+    // +NH, staged per wave at LDS address wbuf and stored with buffer stores
+    // (offsets of rows outside the sequence are out of range, so those stores
+    // are dropped and the count is fixed).
+    __device__ __forceinline__ void epilogue(const PItem& u, int u_wrow0, int u_h, uint32_t wbuf) {
         const float inv = 1.f / (lsum + __shfl_xor(lsum, 32));
         const int64_t base = ((int64_t)(u.s0 + u.q0) * pp->n_heads_q) * D * E::OB;
         const int64_t span = min((int64_t)QT * pp->n_heads_q * D * E::OB, out_bytes - base);
@@ -515,30 +526,30 @@ struct PersistentTask {
         }
     }
 
-    template <int STAGE>
+    // One step of the compute side on ring half HALF: its two tiles landed
+    // (waited here), the next step's tiles go out into the other half.
+    template <int HALF>
     __device__ __forceinline__ void step() {
-        // wait for this tile's loads: everything issued after them may stay in flight
-        const int nst = (end1 != 0) + (end2 != 0), nql = (end1 == 2) + (end2 == 2);
-        if (nst == 0)
-            wait_vmcnt<DMA>();
-        else if (nst == 1)
-            nql == 0 ? wait_vmcnt<DMA + ST>() : wait_vmcnt<DMA + QL + ST>();
-        else if (nql == 0)
-            wait_vmcnt<DMA + 2 * ST>();
+        // wait for this step's tile loads: what the previous step issued after them may stay in flight
+        if (end1 == 0)
+            wait_vmcnt<0>();
+        else if (end1 == 1)
+            wait_vmcnt<ST>();
         else
-            nql == 1 ? wait_vmcnt<DMA + QL + 2 * ST>() : wait_vmcnt<DMA + 2 * QL + 2 * ST>();
+            wait_vmcnt<ST + QL>();
         if (pend && pend_ps <= step_no) publish(step_no);   // the ticket has landed
-        __builtin_amdgcn_s_barrier();           // every wave's loads landed; the previous tile is consumed
-        issue_next<(STAGE + 2) % kStages>(step_no);
+        __builtin_amdgcn_s_barrier();           // every wave's loads landed; the other half is consumed
+        issue_next<1 - HALF>(step_no);
         if (fresh) wait_vmcnt<DMA>();           // this item's Q rows (issued just before this step's tile loads)
 #pragma unroll
         for (int ks = 0; ks < G::NKS; ++ks) pin_after_wait(qreg[ks]);
-        const int k0 = tc * kKT;
-        if (tc <= last_tile) {
-            // one body for both cases (two inlined copies would double the live registers)
-            attend_tile<D, STAGE, true>(lc, 0u, qreg, hf, c, m, lsum, o, k0 + kKT - 1 > wrow0, qrow - k0);
-        }
-        end2 = end1;
+        const int u0 = 2 * tc;                  // this step's first 32-key tile within the item
+        if (u0 <= last_tile)
+            attend_tile<D, 2 * HALF, true>(lc, 0u, qreg, hf, c, m, lsum, o, u0 * kKT + kKT - 1 > wrow0,
+                                           qrow - u0 * kKT);
+        if (u0 + 1 <= last_tile)
+            attend_tile<D, 2 * HALF + 1, true>(lc, 0u, qreg, hf, c, m, lsum, o, (u0 + 1) * kKT + kKT - 1 > wrow0,
+                                               qrow - (u0 + 1) * kKT);
         end1 = 0;
         fresh = false;
         ++step_no;
@@ -561,7 +572,14 @@ struct PersistentTask {
                 cu.h0 = __builtin_amdgcn_readfirstlane(nu.h0);
                 bind();
             }
-            epilogue(fin, fin_wrow0, fin_h);    // ST ops
+            uint32_t wbuf;
+            if constexpr (EPI_IN_RING) {
+                __builtin_amdgcn_s_barrier();   // every wave is done reading this half
+                wbuf = ring_addr + 2 * HALF * G::STAGEB + wave * E::WAVEB;
+            } else {
+                wbuf = ring_addr + 4 * G::STAGEB + wave * E::WAVEB;
+            }
+            epilogue(fin, fin_wrow0, fin_h, wbuf);   // ST ops; its LDS reads have landed before it returns
             if (more) load_q();                 // QL ops, after the stores: qreg is free during the epilogue
             end1 = more ? 2 : 1;
             reset();
@@ -577,14 +595,15 @@ template <int D, int NH, bool OUT_BF16>
 __global__ __launch_bounds__(256, 2) void prefill_persistent_kernel(const PrefillParams p) {
     using G = Geo<D>;
     using E = Epi<D, OUT_BF16>;
-    __shared__ __attribute__((aligned(1024))) char ring[kStages * G::STAGEB + 4 * E::WAVEB];
+    using Task = PersistentTask<D, NH, OUT_BF16>;
+    __shared__ __attribute__((aligned(1024))) char ring[Task::LDS_BYTES];
     __shared__ int slot[1];                     // list index of the next item
 
     const int x = blockIdx.x % kNumXcd, l = blockIdx.x / kNumXcd;
     const int cnt = scalar_load4(p.plan_count + x);
     if (l >= cnt) return;
 
-    PersistentTask<D, NH, OUT_BF16> T;
+    Task T;
     T.pp = &p;
     T.ring = ring;
     T.list = p.plan_items + scalar_load4(p.plan_off + x);
@@ -598,7 +617,7 @@ __global__ __launch_bounds__(256, 2) void prefill_persistent_kernel(const Prefil
     T.c = p.scale_log2;
     T.kv_stride = (int64_t)p.n_heads_kv * D;
     T.out_bytes = (int64_t)p.total_tokens * p.n_heads_q * D * E::OB;
-    T.wbuf = lds_addr(ring) + kStages * G::STAGEB + T.wave * E::WAVEB;
+    T.ring_addr = lds_addr(ring);
     T.slot_addr = lds_addr(slot);
     make_lane_const<D>(T.lc, T.lane, T.wave, lds_addr(ring));
 
@@ -631,20 +650,16 @@ __global__ __launch_bounds__(256, 2) void prefill_persistent_kernel(const Prefil
     T.bind();
     T.reset();
     T.end1 = 0;
-    T.end2 = 0;
     T.fresh = false;
     T.done = false;
     T.step_no = 0;
 
     T.load_q();
-    T.template issue_next<0>(-2);
-    T.template issue_next<1>(-1);
+    T.template issue_next<0>(-1);               // the first step's wait (vmcnt 0) also covers the Q rows
     for (;;) {
         T.template step<0>();
         if (T.done) break;
         T.template step<1>();
-        if (T.done) break;
-        T.template step<2>();
         if (T.done) break;
     }
     wait_vmcnt<0>();                            // loads and tickets issued past the end land before the LDS is released
