@@ -602,6 +602,19 @@ def main():
     gather_us = med(per["gather"])
     search_us = med(per["beam_search"])
     beam_parts = time_beam(ctx, beam, ev, 20)                        # per-launch breakdown, outside the timed steps
+    # the same prefill with bf16 output (half the output bytes), reporting only
+    pout_bf = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        ctx.packed_prefill_attn(q, k, v, cu, pf.max_seqlen, out=pout_bf)
+    bf_ev = []
+    for _ in range(pf.n_layers):
+        e0 = ev()
+        ctx.packed_prefill_attn(q, k, v, cu, pf.max_seqlen, out=pout_bf)
+        bf_ev.append((e0, ev()))
+    torch.cuda.synchronize()
+    ctx.check()
+    bf_us = med([a.elapsed_time(b) * 1e3 for a, b in bf_ev])
+    del pout_bf
 
     pbytes, pflops = prefill_bytes_flops(pf.lengths, Hq, Hkv, D, 4)
     achieved_gbs = pbytes / (prefill_us * 1e-6) / 1e9
@@ -653,6 +666,15 @@ def main():
             "beam_search_one_call_us_in_step": round(search_us, 1),
         }, **beam_parts, host_wall_s=round(t_wall, 3)),
     }
+    bbytes, _ = prefill_bytes_flops(pf.lengths, Hq, Hkv, D, 2)
+    line["prefill_bf16_out"] = {
+        "workload": "the same 960-sequence prefill layer with bf16 output (28 launches, median)",
+        "us_per_layer_median": round(bf_us, 2),
+        "algorithmic_bytes": bbytes,
+        "hbm_frac": round(bbytes / (bf_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(pflops / (bf_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "mfma_frac_ceiling_at_hbm_peak": round(min(1.0, pflops / bbytes * HBM_PEAK_GBS * 1e9 / 1e12
+                                                   / MFMA_BF16_PEAK_TFLOPS), 4)}
     if graph_ms is not None:
         line["graph_replay"] = {"ms_per_step": round(graph_ms, 4),
                                 "tokens_per_s": round(pf.total_tokens / (graph_ms * 1e-3), 1),
