@@ -191,7 +191,7 @@ __device__ __forceinline__ void attend_tile(const LaneConst<D>& lc, uint32_t tba
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = max_halves(tmax);
     // The reference max m may trail the true running max by up to kMaxLag in
     // exponent units: every weight exp2((s - m) c) then stays below 2^kMaxLag,
     // and O and the row sum carry one common factor that the final division

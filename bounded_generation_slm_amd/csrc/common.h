@@ -43,4 +43,17 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// x combined with its value in lane l ^ 32 (the other half of the wave),
+// through v_permlane32_swap: one VALU swap instead of an LDS permute.  Both
+// lanes of a pair get the same bits (r[0] holds the lower half's value, r[1]
+// the upper half's).
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace slm

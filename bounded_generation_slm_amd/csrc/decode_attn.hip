@@ -261,7 +261,7 @@ __global__ __launch_bounds__(NTHR, (D == 64 ? 4 : 2)) void beam_decode_attn_kern
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[kb][i]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            tmax = max_halves(tmax);
             const float mnew = fmaxf(mrun, tmax);  // finite: every chunk holds a prompt key
             if (__ballot((mnew - mrun) * c > kMaxLag) != 0) {   // mrun = -inf on the first chunk: taken
                 const float alpha = fast_exp2((mrun - mnew) * c);
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(NTHR, (D == 64 ? 4 : 2)) void beam_decode_attn_kern
             for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) part = dot2_bf16(qreg[ks][e], kv[ks][e], part);
-            part += __shfl_xor(part, 32);
+            part = sum_halves(part);
             const float s = part * p.scale_log2;
             const float mnew = fmaxf(mrun, s);     // finite: s is
             const float alpha = fast_exp2(mrun - mnew);
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(NTHR, (D == 64 ? 4 : 2)) void beam_decode_attn_kern
                 }
         }
 
-        lsum += __shfl_xor(lsum, 32);
+        lsum = sum_halves(lsum);
         if constexpr (STAGE) {
             // tile [32 rows][kStageRow] floats behind the prompt copy, one per wave
             float* st = (float*)(vt_lds + (size_t)D * VROW) + (size_t)wave * 32 * kStageRow;

@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(const PrefillParam
         tile(t + 2, std::integral_constant<int, 2>{});
     }
     wait_vmcnt<0>();                            // the tiles issued past the end must land
-    lsum += __shfl_xor(lsum, 32);
+    lsum = sum_halves(lsum);
     const float inv = 1.f / lsum;
 
     __builtin_amdgcn_s_barrier();               // every wave is done with the ring
@@ -501,7 +501,7 @@ struct PersistentTask {
     // (offsets of rows outside the sequence are out of range, so those stores
     // are dropped and the count is fixed).
     __device__ __forceinline__ void epilogue(const PItem& u, int u_wrow0, int u_h, uint32_t wbuf) {
-        const float inv = 1.f / (lsum + __shfl_xor(lsum, 32));
+        const float inv = 1.f / sum_halves(lsum);
         const int64_t base = ((int64_t)(u.s0 + u.q0) * pp->n_heads_q) * D * E::OB;
         const int64_t span = min((int64_t)QT * pp->n_heads_q * D * E::OB, out_bytes - base);
         const __amdgpu_buffer_rsrc_t rsrc =
@@ -593,7 +593,6 @@ struct PersistentTask {
 
 template <int D, int NH, bool OUT_BF16>
 __global__ __launch_bounds__(256, 2) void prefill_persistent_kernel(const PrefillParams p) {
-    using G = Geo<D>;
     using E = Epi<D, OUT_BF16>;
     using Task = PersistentTask<D, NH, OUT_BF16>;
     __shared__ __attribute__((aligned(1024))) char ring[Task::LDS_BYTES];
