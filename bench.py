@@ -51,11 +51,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the timed oracle runs")
-    ap.add_argument("--cpu-baseline-full", action="store_true",
-                    help="also time the oracle's whole long-prompt search (about a minute more)")
     ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph timing of the step")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the reporting-only prefill-request and long-prompt beam timings")
+    ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
+                    help="host only: print a summary of rocprofv3 CSV output and exit. KIND is 'trace' (one "
+                         "--kernel-trace dir), 'sq' (--pmc dirs of SQ counters) or 'traffic' (FETCH_SIZE dir, "
+                         "WRITE_SIZE dir, and the same two for --copy-calibration; writes the prefill record)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--kernels-only", action="store_true",
@@ -64,9 +66,16 @@ def parse():
     return ap.parse_args()
 
 
-def src_sha(name: str) -> str:
-    with open(os.path.join(ROOT, "bounded_generation_slm_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+PREFILL_SOURCES = ("prefill_attn.hip", "attn_tile.h")
+
+
+def src_sha(*names: str) -> str:
+    """Short hash of kernel sources (csrc/), to tie a counter record to them."""
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "bounded_generation_slm_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def prefill_bytes_flops(lengths, Hq, Hkv, D, out_bytes):
@@ -141,12 +150,13 @@ def oracle_beam_search_time(run):
     return round(time.perf_counter() - t0, 3)
 
 
-def cpu_baseline(pf, pf_dev, beam):
+def cpu_baseline(pf, pf_dev, beam, more=None):
     """The oracle on the host cores, per workload on the same arrays the GPU
     reads: the tiny workload (prefill and 4-step search), the one-request
     prefill, layer 0 of the 960-sequence pack (the 28 layer calls of a step
-    read one Q/K/V set, so the step's prefill is 28 times that) and the whole
-    short-prompt search.  value: prefill tokens per second of one whole step
+    read one Q/K/V set, so the step's prefill is 28 times that), the whole
+    short-prompt search and (in `more`, timed where its arrays live) the whole
+    long-prompt search.  value: prefill tokens per second of one whole step
     (28 prefill layers + gather + short-prompt search), like the GPU value."""
     import numpy as np
 
@@ -181,6 +191,7 @@ def cpu_baseline(pf, pf_dev, beam):
     per["prefill_throughput 28 layers (extrapolated: 28 x layer 0)"] = round(t_layer * pf.n_layers, 3)
     t_search = oracle_beam_search_time(beam)
     per["beam_short_prompt whole search (R32 x W100, 4 steps, 24 layers)"] = t_search
+    per.update(more or {})
     step_s = t_layer * pf.n_layers + t_gather + t_search
     cpu_model = "unknown"
     try:
@@ -201,24 +212,199 @@ def cpu_baseline(pf, pf_dev, beam):
                  "one_thread_s": one_thread_times()},
         "sample": ("fp64 C oracle, %d threads, on the bench's own arrays: prefill layer 0 of the 960-sequence pack "
                    "in full (%.1f s, x28 for the step's 28 layer calls over the same Q/K/V), the gather, and the whole "
-                   "short-prompt search in full (%.1f s); one step estimated at %.0f s" % (
+                   "short-prompt search in full (%.1f s); one step estimated at %.0f s. The long-prompt search, "
+                   "timed in full, is listed per workload (not part of value)" % (
                        threads, t_layer, t_search, step_s)),
     }
 
 
-def traffic_from_counters(kernel_file: str, launch_bytes_key: str):
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel source."""
+def traffic_from_counters(launch_bytes_key: str):
+    """HBM bytes per launch from the committed counter record, if it was
+    taken on the current prefill kernel sources."""
     path = os.path.join(PROFILES, "prefill_attn_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_sha") != src_sha(kernel_file):
+    if rec.get("kernel_source_sha") != src_sha(*PREFILL_SOURCES):
         return None
     return rec.get(launch_bytes_key)
 
 
-def extra_workloads(ctx, dev, ev, reps=5, full_cpu=False):
+# ---------------------------------------------------------------------------
+# rocprofv3 output -> the text summaries kept under profiles/ (runs on the
+# host, on the CSV files a profiled run of this script wrote)
+
+N_XCD, N_SIMD = 8, 256 * 4          # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def _kernel_short(name: str) -> str:
+    import re
+    name = name.replace("void ", "").replace("slm::(anonymous namespace)::", "slm::")
+    return re.sub(r"\((slm::)?\w+Params.*\)$", "", name)
+
+
+def _csv_rows(d: str, suffix: str):
+    import csv
+    import glob
+    out = []
+    for path in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        with open(path, newline="") as f:
+            out += list(csv.DictReader(f))
+    return out
+
+
+def _dispatch_counters(d: str):
+    """{dispatch id: (kernel, grid, duration ns, {counter: value})} of one
+    --pmc run (a counter's per-instance rows summed)."""
+    disp = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        key = int(r["Dispatch_Id"])
+        k = disp.setdefault(key, [r["Kernel_Name"], int(r["Grid_Size"]),
+                                  int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), {}])
+        k[3][r["Counter_Name"]] = k[3].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return disp
+
+
+def _groups(disp, only_slm=True):
+    """Per (kernel, grid): number of dispatches, mean duration and mean counters."""
+    g = {}
+    for kern, grid, dur, cs in disp.values():
+        if only_slm and "slm::" not in kern:
+            continue
+        e = g.setdefault((kern, grid), {"n": 0, "dur": 0.0, "c": {}})
+        e["n"] += 1
+        e["dur"] += dur
+        for c, v in cs.items():
+            e["c"][c] = e["c"].get(c, 0.0) + v
+    for e in g.values():
+        e["dur"] /= e["n"]
+        e["c"] = {c: v / e["n"] for c, v in e["c"].items()}
+    return g
+
+
+def summarize_kernel_trace(d: str) -> str:
+    """Per (kernel, grid) launch statistics from a --kernel-trace run."""
+    g = {}
+    for r in _csv_rows(d, "kernel_trace.csv"):
+        key = (r["Kernel_Name"], int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0))
+        g.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    total = sum(sum(v) for v in g.values()) or 1
+    lines = ["# calls  avg_us   min_us   max_us   share  grid  kernel"]
+    for (kern, grid), v in sorted(g.items(), key=lambda kv: -sum(kv[1])):
+        lines.append("%6d %8.1f %8.1f %8.1f %6.2f%% %7d  %s" % (
+            len(v), sum(v) / len(v) / 1e3, min(v) / 1e3, max(v) / 1e3, 100.0 * sum(v) / total, grid,
+            _kernel_short(kern)[:110]))
+    return "\n".join(lines)
+
+
+def summarize_sq(dirs) -> str:
+    """Instruction mix and MFMA use per (kernel, grid) from --pmc runs of SQ
+    counters.  Normalisation: GRBM_GUI_ACTIVE is the sum of the 8 XCDs'
+    busy-cycle counters (divided by 8 it gives the clock over the dispatch);
+    SQ_VALU_MFMA_BUSY_CYCLES is summed over all SIMDs, so the MFMA-busy
+    fraction is busy / (cycles x 1024 SIMDs)."""
+    merged = {}
+    for d in dirs:
+        for key, e in _groups(_dispatch_counters(d)).items():
+            m = merged.setdefault(key, {"n": e["n"], "dur": e["dur"], "c": {}})
+            m["c"].update(e["c"])
+    lines = []
+    for (kern, grid), e in sorted(merged.items(), key=lambda kv: -kv[1]["dur"] * kv[1]["n"]):
+        c = e["c"]
+        waves = c.get("SQ_WAVES", 0.0) or 1.0
+        mfma = c.get("SQ_INSTS_MFMA", 0.0)
+        cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
+        row = {"dispatches": e["n"], "grid": grid, "us_profiled": round(e["dur"] / 1e3, 1),
+               "clock_GHz": round(cyc / e["dur"], 3) if cyc else None, "waves": int(waves)}
+        for name, cnt in (("VALU", "SQ_INSTS_VALU"), ("SALU", "SQ_INSTS_SALU"), ("MFMA", "SQ_INSTS_MFMA"),
+                          ("LDS", "SQ_INSTS_LDS"), ("VMEM_RD", "SQ_INSTS_VMEM_RD"), ("SMEM", "SQ_INSTS_SMEM")):
+            if cnt in c:
+                row[name + "_per_wave"] = round(c[cnt] / waves, 1)
+        if mfma:
+            row["VALU_per_MFMA"] = round(c.get("SQ_INSTS_VALU", 0.0) / mfma, 2)
+            row["SALU_per_MFMA"] = round(c.get("SQ_INSTS_SALU", 0.0) / mfma, 2)
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                row["MFMA_busy_cycles_per_inst"] = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / mfma, 2)
+        if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            row["MFMA_busy_frac"] = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * N_SIMD), 4)
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:         # units of 512 flops
+            row["MFMA_bf16_TFLOP_executed"] = round(c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / 1e12, 4)
+        wc = c.get("SQ_WAVE_CYCLES")
+        if wc:
+            for name, cnt in (("wait_any", "SQ_WAIT_INST_ANY"), ("active_valu", "SQ_ACTIVE_INST_VALU"),
+                              ("active_lds", "SQ_ACTIVE_INST_LDS"), ("active_any", "SQ_ACTIVE_INST_ANY")):
+                if cnt in c:
+                    row[name + "_per_wave_cycle"] = round(c[cnt] / wc, 3)
+        if c.get("SQ_ACTIVE_INST_LDS") and "SQ_LDS_BANK_CONFLICT" in c:
+            row["lds_bank_conflict_per_lds_cycle"] = round(c["SQ_LDS_BANK_CONFLICT"] / c["SQ_ACTIVE_INST_LDS"], 3)
+        lines.append(_kernel_short(kern))
+        lines.append("    " + json.dumps(row))
+    return "\n".join(lines)
+
+
+def summarize_traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, record=None) -> str:
+    """HBM bytes per dispatch from FETCH_SIZE and WRITE_SIZE (KiB) runs,
+    each scaled by what the same counter reads for a plain device copy of
+    known size (bench.py --copy-calibration).  With `record`, also writes the
+    prefill call's bytes (plan + persistent kernel, fp32 out on the
+    960-sequence pack) as JSON for the bench's roofline.traffic."""
+    copy_bytes = (1 << 28) * 4
+
+    def copy_kib(d, cnt):
+        best = 0.0
+        for kern, grid, dur, cs in _dispatch_counters(d).values():
+            if "slm::" not in kern:
+                best = max(best, cs.get(cnt, 0.0))
+        return best
+
+    fs = copy_bytes / 1024.0 / copy_kib(cal_fetch_dir, "FETCH_SIZE")
+    ws = copy_bytes / 1024.0 / copy_kib(cal_write_dir, "WRITE_SIZE")
+    fg, wg = _groups(_dispatch_counters(fetch_dir)), _groups(_dispatch_counters(write_dir))
+    lines = ["# copy calibration: %d bytes each way; FETCH_SIZE scale %.4f, WRITE_SIZE scale %.4f" % (
+        copy_bytes, fs, ws),
+        "# dispatches  grid  FETCH_KiB_raw  WRITE_KiB_raw  read_GB  write_GB  kernel"]
+    for key in sorted(set(fg) | set(wg), key=lambda k: -(fg.get(k, {}).get("c", {}).get("FETCH_SIZE", 0.0))):
+        f = fg.get(key, {}).get("c", {}).get("FETCH_SIZE", 0.0)
+        w = wg.get(key, {}).get("c", {}).get("WRITE_SIZE", 0.0)
+        n = fg.get(key, wg.get(key, {})).get("n", 0)
+        lines.append("%6d %8d %14.1f %14.1f %8.3f %8.3f  %s" % (
+            n, key[1], f, w, f * fs * 1024 / 1e9, w * ws * 1024 / 1e9, _kernel_short(key[0])[:100]))
+    if record:
+        import workloads as wl
+        pf = wl.PREFILL_THROUGHPUT
+        per = {"persistent_fetch": 0.0, "persistent_write": 0.0, "plan_fetch": 0.0, "plan_write": 0.0}
+        n = 0
+        for (kern, grid), e in fg.items():
+            if "prefill_persistent_kernel<128, 2, false>" in kern:
+                per["persistent_fetch"], n = e["c"].get("FETCH_SIZE", 0.0), e["n"]
+            elif "prefill_plan_kernel" in kern:
+                per["plan_fetch"] = e["c"].get("FETCH_SIZE", 0.0)
+        for (kern, grid), e in wg.items():
+            if "prefill_persistent_kernel<128, 2, false>" in kern:
+                per["persistent_write"] = e["c"].get("WRITE_SIZE", 0.0)
+            elif "prefill_plan_kernel" in kern:
+                per["plan_write"] = e["c"].get("WRITE_SIZE", 0.0)
+        hbm = (per["persistent_fetch"] + per["plan_fetch"]) * fs * 1024 + \
+            (per["persistent_write"] + per["plan_write"]) * ws * 1024
+        alg, _ = prefill_bytes_flops(pf.lengths, pf.n_heads_q, pf.n_heads_kv, pf.head_dim, 4)
+        rec = {"kernel_source_sha": src_sha(*PREFILL_SOURCES),
+               "what": "HBM bytes of one packed-prefill call (prefill_plan_kernel + "
+                       "prefill_persistent_kernel<128,2,f32>) on the 960-sequence pack (T=%d, Hq16/Hkv8/D128, "
+                       "fp32 out)" % pf.total_tokens,
+               "calibration": {"copy_bytes_each_way": copy_bytes, "fetch_scale": round(fs, 4),
+                               "write_scale": round(ws, 4)},
+               "per_dispatch_kib": dict({k: round(v, 1) for k, v in per.items()}, dispatches=n),
+               "hbm_bytes_per_launch": int(round(hbm)),
+               "algorithmic_bytes_per_launch": alg}
+        with open(record, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        lines.append("# prefill call: %.4f GB counted vs %.4f GB algorithmic (x%.4f)" % (hbm / 1e9, alg / 1e9,
+                                                                                    hbm / alg))
+    return "\n".join(lines)
+
+
+def extra_workloads(ctx, dev, ev, reps=5, cpu_oracle=True):
     """Reporting-only timings outside the timed step (not part of value)."""
     import torch
     import workloads as wl
@@ -282,8 +468,8 @@ def extra_workloads(ctx, dev, ev, reps=5, full_cpu=False):
     bl.run(ctx)
     res["beam_long_prompt"] = dict(
         {"workload": "R8 x W400, P480, 5 steps, 24 layers, Hq14/Hkv2/D64, V151936"}, **time_beam(ctx, bl, ev, 20))
-    if full_cpu:
-        res["beam_long_prompt"]["cpu_oracle"] = oracle_beam_search_time(bl)
+    if cpu_oracle:                  # moved into cpu_baseline by the caller
+        res["oracle_long_search_s"] = oracle_beam_search_time(bl)
     del bl
     torch.cuda.empty_cache()
     # beam-search prompt prefill: R equal-length prompts packed, K/V kept in
@@ -478,6 +664,17 @@ def time_beam(ctx, run, ev, reps):
 
 def main():
     args = parse()
+    if args.summarize:
+        kind, dirs = args.summarize[0], args.summarize[1:]
+        if kind == "trace" and len(dirs) == 1:
+            print(summarize_kernel_trace(dirs[0]))
+        elif kind == "sq" and dirs:
+            print(summarize_sq(dirs))
+        elif kind == "traffic" and len(dirs) == 4:
+            print(summarize_traffic(*dirs, record=os.path.join(PROFILES, "prefill_attn_traffic.json")))
+        else:
+            sys.exit("bench.py --summarize: trace DIR | sq DIR... | traffic FETCH WRITE CAL_FETCH CAL_WRITE")
+        return
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the path shards by sequence / request "
               "with no exchange); --gpus %d is not run" % args.gpus, file=sys.stderr)
@@ -619,8 +816,9 @@ def main():
     pbytes, pflops = prefill_bytes_flops(pf.lengths, Hq, Hkv, D, 4)
     achieved_gbs = pbytes / (prefill_us * 1e-6) / 1e9
     mfma_tflops = pflops / (prefill_us * 1e-6) / 1e12
-    traffic = traffic_from_counters("prefill_attn.hip", "hbm_bytes_per_launch")
-    extra = {} if args.no_extra else extra_workloads(ctx, dev, ev, full_cpu=args.cpu_baseline_full)
+    traffic = traffic_from_counters("hbm_bytes_per_launch")
+    extra = {} if args.no_extra else extra_workloads(ctx, dev, ev, cpu_oracle=not args.no_cpu_baseline)
+    long_s = extra.get("reporting_only", {}).pop("oracle_long_search_s", None)
 
     value = pf.total_tokens / (ms_step * 1e-3)
     line = {
@@ -681,7 +879,8 @@ def main():
                                 "what": "the same step captured once as a HIP graph and replayed"}
     line.update(extra)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(pf, (q, k, v, hidden), beam)
+        more = {} if long_s is None else {"beam_long_prompt whole search (R8 x W400, 5 steps, 24 layers)": long_s}
+        line["cpu_baseline"] = cpu_baseline(pf, (q, k, v, hidden), beam, more)
     print(json.dumps(line), flush=True)
 
 
