@@ -39,7 +39,7 @@ EXPORTED = (
     "slm_ctx_set_stream", "slm_ctx_check", "slm_ctx_last_error", "slm_packed_prefill_attn",
     "slm_gather_last", "slm_beam_decode_attn", "slm_beam_topk_merge", "slm_beam_topk_merge_logits",
     "slm_beam_reorder_suffix", "slm_label_head", "slm_beam_backtrack", "slm_beam_search",
-    "slm_packed_prefill_attn_noalloc",
+    "slm_packed_prefill_attn_noalloc", "slm_prefill_plan", "slm_packed_prefill_attn_planned",
 )
 
 
@@ -72,7 +72,7 @@ class _BeamSearchArgs(ctypes.Structure):
 
 _P, _I, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
 _lib.slm_abi_version.restype = ctypes.c_int
-_ABI = 5                                  # the struct layouts above and the symbol set
+_ABI = 6                                  # the struct layouts above and the symbol set
 if _lib.slm_abi_version() != _ABI:
     raise ImportError("%s has ABI version %d, this binding expects %d: rebuild it with "
                       "bounded_generation_slm_amd/_build.py" % (LIB_PATH, _lib.slm_abi_version(), _ABI))
@@ -95,6 +95,9 @@ _lib.slm_beam_reorder_suffix.argtypes = [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P,
 _lib.slm_beam_backtrack.argtypes = [_P, _P, _P, _I, _I, _I, _P]
 _lib.slm_beam_search.argtypes = [_P, ctypes.POINTER(_BeamSearchArgs)]
 _lib.slm_packed_prefill_attn_noalloc.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, ctypes.c_int, _P]
+_lib.slm_prefill_plan.argtypes = [_P, _P, _I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_uint64)]
+_lib.slm_packed_prefill_attn_planned.argtypes = [_P, ctypes.c_uint64, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P,
+                                                 ctypes.c_int]
 for _name in ("slm_ctx_create", "slm_ctx_set_stream", "slm_ctx_check", "slm_packed_prefill_attn",
               "slm_gather_last", "slm_beam_decode_attn", "slm_beam_topk_merge", "slm_beam_topk_merge_logits",
               "slm_beam_reorder_suffix", "slm_label_head", "slm_beam_backtrack", "slm_beam_search",
@@ -187,6 +190,15 @@ class Context:
                             out: Optional[torch.Tensor] = None, out_dtype=torch.float32):
         return slm_packed_prefill_attn(self, q, k, v, cu_seqlens, max_seqlen, scale, out, out_dtype)
 
+    def prefill_plan(self, cu_seqlens, max_seqlen: int, total_tokens: int, n_heads_q: int, n_heads_kv: int,
+                     head_dim: int) -> int:
+        return slm_prefill_plan(self, cu_seqlens, max_seqlen, total_tokens, n_heads_q, n_heads_kv, head_dim)
+
+    def packed_prefill_attn_planned(self, plan: int, q, k, v, cu_seqlens, max_seqlen: int,
+                                    scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                                    out_dtype=torch.float32):
+        return slm_packed_prefill_attn_planned(self, plan, q, k, v, cu_seqlens, max_seqlen, scale, out, out_dtype)
+
     def gather_last(self, hidden, cu_seqlens, out=None):
         return slm_gather_last(self, hidden, cu_seqlens, out)
 
@@ -241,6 +253,32 @@ def slm_packed_prefill_attn(ctx: Context, q, k, v, cu_seqlens, max_seqlen: int,
                             out_dtype=torch.float32) -> torch.Tensor:
     """q [T,Hq,D], k/v [T,Hkv,D] bf16; cu_seqlens [B+1] int32 (device).
     Returns out [T,Hq,D] (float32 or bfloat16)."""
+    return _prefill(ctx, None, q, k, v, cu_seqlens, max_seqlen, scale, out, out_dtype)
+
+
+def slm_prefill_plan(ctx: Context, cu_seqlens, max_seqlen: int, total_tokens: int, n_heads_q: int,
+                     n_heads_kv: int, head_dim: int) -> int:
+    """The work list of the pack cu_seqlens [B+1] int32 (device) with these
+    sizes, built on the device; returns the plan id for
+    slm_packed_prefill_attn_planned (the context's one current plan)."""
+    dev = ctx.device
+    plan = ctypes.c_uint64(0)
+    ctx._stream()
+    rc = _lib.slm_prefill_plan(ctx._h, _ptr(cu_seqlens, "cu_seqlens", (torch.int32,), dev), cu_seqlens.numel() - 1,
+                               int(total_tokens), int(max_seqlen), int(n_heads_q), int(n_heads_kv), int(head_dim),
+                               ctypes.byref(plan))
+    ctx._raise(rc, "slm_prefill_plan")
+    return plan.value
+
+
+def slm_packed_prefill_attn_planned(ctx: Context, plan: int, q, k, v, cu_seqlens, max_seqlen: int,
+                                    scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                                    out_dtype=torch.float32) -> torch.Tensor:
+    """slm_packed_prefill_attn over the plan `plan` (same cu_seqlens and sizes)."""
+    return _prefill(ctx, int(plan), q, k, v, cu_seqlens, max_seqlen, scale, out, out_dtype)
+
+
+def _prefill(ctx: Context, plan, q, k, v, cu_seqlens, max_seqlen, scale, out, out_dtype) -> torch.Tensor:
     dev = ctx.device
     T, Hq, D = q.shape
     Hkv = k.shape[1]
@@ -252,11 +290,13 @@ def slm_packed_prefill_attn(ctx: Context, q, k, v, cu_seqlens, max_seqlen: int,
         raise ValueError("out must be [T, Hq, D] float32 or bfloat16")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     ctx._stream()
-    rc = _lib.slm_packed_prefill_attn(
-        ctx._h, _ptr(q, "q", _BF16, dev), _ptr(k, "k", _BF16, dev), _ptr(v, "v", _BF16, dev),
-        _ptr(cu_seqlens, "cu_seqlens", (torch.int32,), dev), cu_seqlens.numel() - 1, T,
-        int(max_seqlen), Hq, Hkv, D, scale, _ptr(out, "out", tuple(_OUT), dev), _OUT[out.dtype])
-    ctx._raise(rc, "slm_packed_prefill_attn")
+    args = (_ptr(q, "q", _BF16, dev), _ptr(k, "k", _BF16, dev), _ptr(v, "v", _BF16, dev),
+            _ptr(cu_seqlens, "cu_seqlens", (torch.int32,), dev), cu_seqlens.numel() - 1, T,
+            int(max_seqlen), Hq, Hkv, D, scale, _ptr(out, "out", tuple(_OUT), dev), _OUT[out.dtype])
+    if plan is None:
+        ctx._raise(_lib.slm_packed_prefill_attn(ctx._h, *args), "slm_packed_prefill_attn")
+    else:
+        ctx._raise(_lib.slm_packed_prefill_attn_planned(ctx._h, plan, *args), "slm_packed_prefill_attn_planned")
     return out
 
 

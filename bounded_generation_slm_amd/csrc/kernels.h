@@ -48,11 +48,16 @@ struct PrefillParams {
     int4* plan_items;                   // {s0, L, unit in sequence, query tile}
     int* plan_count;                    // [8] units per XCD
     int* plan_off;                      // [8] first unit of each XCD in plan_items
-    int* plan_claim;                    // [8] per-XCD item counters (zeroed by the plan kernel)
+    int* plan_claim;                    // [8] per-XCD item counters
+    int* plan_done;                     // [8] per-XCD finished-workgroup counters; the plan kernel zeroes
+                                        // both, and the last workgroup of each run zeroes them again
     int plan_cap;                       // capacity of plan_items
 };
+// Prefill phases: the work list of a pack (persistent form only) and the
+// attention over it; a plan serves any number of runs over the same pack.
+constexpr int kPrefillPlan = 1, kPrefillRun = 2;
 hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, bool out_bf16, bool persistent,
-                               int num_cus, LaunchCache& cache, hipStream_t stream);
+                               int num_cus, LaunchCache& cache, hipStream_t stream, int phases);
 // the persistent form stages cu_seqlens in LDS: packs of fewer sequences only
 constexpr int kPrefillPlanMaxSeqs = 15999;
 // plan entries a pack can need: sum over sequences of ceil(L / qt_rows), per unit column

@@ -257,6 +257,7 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const Prefil
         p.plan_count[x] = tot[x];
         p.plan_off[x] = pos0;
         p.plan_claim[x] = 0;
+        p.plan_done[x] = 0;
     }
     const int n_mine = (p.n_units - x + kNumXcd - 1) / kNumXcd;   // units x, x + 8, ...
     for (int base = 0; base < n_mine; base += kPlanThreads) {
@@ -666,6 +667,14 @@ __global__ __launch_bounds__(256, 2) void prefill_persistent_kernel(const Prefil
         if (T.done) break;
     }
     wait_vmcnt<0>();                            // loads and tickets issued past the end land before the LDS is released
+    // The XCD's counters start the next run over the same plan at zero: every
+    // active workgroup counts itself out once its last ticket has returned
+    // (waited just above), and the last one clears both counters.  Exactly
+    // min(workgroups per XCD, items) workgroups take part.
+    if (threadIdx.x == 0 && atomicAdd(p.plan_done + x, 1) == min(T.wx, cnt) - 1) {
+        p.plan_claim[x] = 0;
+        p.plan_done[x] = 0;
+    }
 }
 
 template <int D, int NH, bool OUT_BF16>
@@ -680,7 +689,8 @@ hipError_t launch_variant(const PrefillParams& p, hipStream_t stream) {
 }
 
 template <int D, int NH, bool OUT_BF16>
-hipError_t launch_persistent(const PrefillParams& p, int num_cus, LaunchCache& cache, hipStream_t stream) {
+hipError_t launch_persistent(const PrefillParams& p, int num_cus, LaunchCache& cache, hipStream_t stream,
+                             int phases) {
     int& per_cu = cache.prefill_per_cu[D == 128][NH == 2][OUT_BF16];   // resident workgroups per CU
     if (per_cu == 0) {
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
@@ -688,37 +698,43 @@ hipError_t launch_persistent(const PrefillParams& p, int num_cus, LaunchCache& c
         if (e != hipSuccess || per_cu <= 0) per_cu = 1;
     }
     const int grid = max(kNumXcd, per_cu * num_cus / kNumXcd * kNumXcd);
-    const size_t plan_lds = sizeof(int) * ((size_t)p.num_seqs + 1);   // num_seqs < kPrefillPlanMaxSeqs
-    hipLaunchKernelGGL(prefill_plan_kernel, dim3(kNumXcd), dim3(kPlanThreads), plan_lds, stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_persistent_kernel<D, NH, OUT_BF16>), dim3(grid), dim3(256), 0, stream, p);
-    return hipGetLastError();
+    if (phases & kPrefillPlan) {
+        const size_t plan_lds = sizeof(int) * ((size_t)p.num_seqs + 1);   // num_seqs < kPrefillPlanMaxSeqs
+        hipLaunchKernelGGL(prefill_plan_kernel, dim3(kNumXcd), dim3(kPlanThreads), plan_lds, stream, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (phases & kPrefillRun) {
+        hipLaunchKernelGGL((prefill_persistent_kernel<D, NH, OUT_BF16>), dim3(grid), dim3(256), 0, stream, p);
+        return hipGetLastError();
+    }
+    return hipSuccess;
 }
 
 template <int D, int NH, bool OUT_BF16>
-hipError_t dispatch(const PrefillParams& p, bool persistent, int num_cus, LaunchCache& cache, hipStream_t stream) {
-    return persistent ? launch_persistent<D, NH, OUT_BF16>(p, num_cus, cache, stream)
-                      : launch_variant<D, NH, OUT_BF16>(p, stream);
+hipError_t dispatch(const PrefillParams& p, bool persistent, int num_cus, LaunchCache& cache, hipStream_t stream,
+                    int phases) {
+    if (persistent) return launch_persistent<D, NH, OUT_BF16>(p, num_cus, cache, stream, phases);
+    return (phases & kPrefillRun) ? launch_variant<D, NH, OUT_BF16>(p, stream) : hipSuccess;   // no plan to build
 }
 
 }  // namespace
 
 hipError_t launch_prefill_attn(const PrefillParams& p, int head_dim, bool out_bf16, bool persistent, int num_cus,
-                               LaunchCache& cache, hipStream_t stream) {
+                               LaunchCache& cache, hipStream_t stream, int phases) {
     const int nh = p.heads_per_block;
     if (head_dim == 128) {
         if (nh == 2)
-            return out_bf16 ? dispatch<128, 2, true>(p, persistent, num_cus, cache, stream)
-                            : dispatch<128, 2, false>(p, persistent, num_cus, cache, stream);
-        return out_bf16 ? dispatch<128, 1, true>(p, persistent, num_cus, cache, stream)
-                        : dispatch<128, 1, false>(p, persistent, num_cus, cache, stream);
+            return out_bf16 ? dispatch<128, 2, true>(p, persistent, num_cus, cache, stream, phases)
+                            : dispatch<128, 2, false>(p, persistent, num_cus, cache, stream, phases);
+        return out_bf16 ? dispatch<128, 1, true>(p, persistent, num_cus, cache, stream, phases)
+                        : dispatch<128, 1, false>(p, persistent, num_cus, cache, stream, phases);
     }
     if (nh == 2)
-        return out_bf16 ? dispatch<64, 2, true>(p, persistent, num_cus, cache, stream)
-                        : dispatch<64, 2, false>(p, persistent, num_cus, cache, stream);
-    return out_bf16 ? dispatch<64, 1, true>(p, persistent, num_cus, cache, stream)
-                    : dispatch<64, 1, false>(p, persistent, num_cus, cache, stream);
+        return out_bf16 ? dispatch<64, 2, true>(p, persistent, num_cus, cache, stream, phases)
+                        : dispatch<64, 2, false>(p, persistent, num_cus, cache, stream, phases);
+    return out_bf16 ? dispatch<64, 1, true>(p, persistent, num_cus, cache, stream, phases)
+                    : dispatch<64, 1, false>(p, persistent, num_cus, cache, stream, phases);
 }
 
 }  // namespace slm

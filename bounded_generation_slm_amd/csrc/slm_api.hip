@@ -37,6 +37,20 @@ struct slm_ctx {
     int topk_blocks_per_cu[slm::kTopkMaxWidth + 1] = {0};   // stage-1 occupancy per width (0 = not queried)
     int topk_logits_blocks_per_cu[slm::kTopkMaxWidth + 1] = {0};   // the same, merge on logits
     slm::LaunchCache launch_cache;  // occupancy and LDS limits of the attention kernels on this device
+    // the current prefill plan: the pack its work list was built for, and its id
+    // (every call that rewrites the work list moves plan_gen on)
+    struct PlanKey {
+        const int32_t* cu;
+        int32_t num_seqs, total_tokens, max_seqlen, n_heads_q, n_heads_kv, head_dim;
+        bool operator==(const PlanKey& o) const {
+            return cu == o.cu && num_seqs == o.num_seqs && total_tokens == o.total_tokens &&
+                   max_seqlen == o.max_seqlen && n_heads_q == o.n_heads_q && n_heads_kv == o.n_heads_kv &&
+                   head_dim == o.head_dim;
+        }
+    };
+    uint64_t plan_gen = 0;
+    bool plan_valid = false;
+    PlanKey plan_key{};
     char last_error[512] = {0};
 };
 
@@ -217,44 +231,64 @@ slm_status slm_ctx_check(slm_ctx* ctx) {
     return ok(ctx);
 }
 
-slm_status slm_packed_prefill_attn(slm_ctx* ctx, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                   const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
-                                   int32_t max_seqlen, int32_t n_heads_q, int32_t n_heads_kv,
-                                   int32_t head_dim, float scale, void* out, slm_dtype out_dtype) {
+namespace {
+
+enum PrefillMode { kPrefillFull, kPrefillPlanOnly, kPrefillRunOnly };
+
+// Packed prefill in three forms: work list and attention (slm_packed_prefill_attn),
+// the work list alone (slm_prefill_plan), the attention over the current plan
+// (slm_packed_prefill_attn_planned).  The plan form takes no tensors.
+slm_status prefill_call(slm_ctx* ctx, PrefillMode mode, uint64_t plan_id, uint64_t* plan_out, const uint16_t* q,
+                        const uint16_t* k, const uint16_t* v, const int32_t* cu_seqlens, int32_t num_seqs,
+                        int32_t total_tokens, int32_t max_seqlen, int32_t n_heads_q, int32_t n_heads_kv,
+                        int32_t head_dim, float scale, void* out, slm_dtype out_dtype) {
     slm_status s = enter(ctx);
     if (s != SLM_OK) return s;
+    const bool tensors = mode != kPrefillPlanOnly;
+    if (mode == kPrefillPlanOnly && !plan_out) return fail(ctx, SLM_ERR_INVALID_ARG, "prefill plan: plan is NULL");
     if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0 || n_heads_q <= 0 || n_heads_kv <= 0 || head_dim <= 0)
         return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: negative size or non-positive head count / head_dim");
     if (n_heads_q % n_heads_kv != 0)
         return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: n_heads_q %% n_heads_kv != 0");
     if (head_dim != 64 && head_dim != 128)
         return fail(ctx, SLM_ERR_UNSUPPORTED, "prefill: head_dim %d (supported: 64, 128)", head_dim);
-    if (out_dtype != SLM_F32 && out_dtype != SLM_BF16)
+    if (tensors && out_dtype != SLM_F32 && out_dtype != SLM_BF16)
         return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: unknown out_dtype");
-    if (!(scale > 0.f) || !std::isfinite(scale))
+    if (tensors && (!(scale > 0.f) || !std::isfinite(scale)))
         return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: scale must be finite and positive");
     if (!cu_seqlens) return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: cu_seqlens is NULL");
     if (max_seqlen == 0 && total_tokens > 0)
         return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: max_seqlen 0 with %d packed tokens", total_tokens);
-    if (total_tokens == 0 || num_seqs == 0) return ok(ctx);
-    if (!q || !k || !v || !out) return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: NULL tensor");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-        return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: tensors must be 16-byte aligned");
-    if (max_seqlen > total_tokens)
-        return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: max_seqlen %d > total_tokens %d", max_seqlen, total_tokens);
-    if (total_tokens > ctx->caps.max_tokens || num_seqs > ctx->caps.max_seqs || n_heads_q > ctx->caps.max_heads_q)
-        return fail(ctx, SLM_ERR_CAPACITY, "prefill: beyond the context caps (tokens %d, seqs %d, heads %d)",
-                    ctx->caps.max_tokens, ctx->caps.max_seqs, ctx->caps.max_heads_q);
-    if (slm::prefill_plan_entries(total_tokens, num_seqs, n_heads_q) > ctx->plan_cap)
-        return fail(ctx, SLM_ERR_CAPACITY, "prefill: the pack's work list (%lld entries) exceeds the workspace (%d)",
-                    (long long)slm::prefill_plan_entries(total_tokens, num_seqs, n_heads_q), ctx->plan_cap);
-    const size_t T = (size_t)total_tokens, D = (size_t)head_dim;
-    const size_t qb = T * n_heads_q * D * 2, kb = T * n_heads_kv * D * 2;
-    const size_t ob = T * n_heads_q * D * (out_dtype == SLM_F32 ? 4 : 2);
-    const size_t cb = ((size_t)num_seqs + 1) * 4;
-    if (overlaps(out, ob, q, qb) || overlaps(out, ob, k, kb) || overlaps(out, ob, v, kb) ||
-        overlaps(out, ob, cu_seqlens, cb))
-        return fail(ctx, SLM_ERR_ALIAS, "prefill: out overlaps an input");
+    const slm_ctx::PlanKey key{cu_seqlens, num_seqs, total_tokens, max_seqlen, n_heads_q, n_heads_kv, head_dim};
+    if (mode == kPrefillRunOnly && !(ctx->plan_valid && plan_id == ctx->plan_gen && key == ctx->plan_key))
+        return fail(ctx, SLM_ERR_INVALID_ARG,
+                    "prefill: plan %llu is not the context's current plan for this cu_seqlens and these sizes",
+                    (unsigned long long)plan_id);
+    const bool empty = total_tokens == 0 || num_seqs == 0;
+    if (!empty) {
+        if (tensors && (!q || !k || !v || !out)) return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: NULL tensor");
+        if (tensors && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)))
+            return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: tensors must be 16-byte aligned");
+        if (max_seqlen > total_tokens)
+            return fail(ctx, SLM_ERR_INVALID_ARG, "prefill: max_seqlen %d > total_tokens %d", max_seqlen,
+                        total_tokens);
+        if (total_tokens > ctx->caps.max_tokens || num_seqs > ctx->caps.max_seqs || n_heads_q > ctx->caps.max_heads_q)
+            return fail(ctx, SLM_ERR_CAPACITY, "prefill: beyond the context caps (tokens %d, seqs %d, heads %d)",
+                        ctx->caps.max_tokens, ctx->caps.max_seqs, ctx->caps.max_heads_q);
+        if (slm::prefill_plan_entries(total_tokens, num_seqs, n_heads_q) > ctx->plan_cap)
+            return fail(ctx, SLM_ERR_CAPACITY,
+                        "prefill: the pack's work list (%lld entries) exceeds the workspace (%d)",
+                        (long long)slm::prefill_plan_entries(total_tokens, num_seqs, n_heads_q), ctx->plan_cap);
+        if (tensors) {
+            const size_t T = (size_t)total_tokens, D = (size_t)head_dim;
+            const size_t qb = T * n_heads_q * D * 2, kb = T * n_heads_kv * D * 2;
+            const size_t ob = T * n_heads_q * D * (out_dtype == SLM_F32 ? 4 : 2);
+            const size_t cb = ((size_t)num_seqs + 1) * 4;
+            if (overlaps(out, ob, q, qb) || overlaps(out, ob, k, kb) || overlaps(out, ob, v, kb) ||
+                overlaps(out, ob, cu_seqlens, cb))
+                return fail(ctx, SLM_ERR_ALIAS, "prefill: out overlaps an input");
+        }
+    }
     slm::PrefillParams p{};
     p.q = q; p.k = k; p.v = v; p.cu = cu_seqlens; p.out = out; p.err = ctx->err_flag;
     p.num_seqs = num_seqs; p.total_tokens = total_tokens; p.max_seqlen = max_seqlen;
@@ -272,12 +306,48 @@ slm_status slm_packed_prefill_attn(slm_ctx* ctx, const uint16_t* q, const uint16
     p.plan_count = (int*)(ctx->plan_items + ctx->plan_cap);
     p.plan_off = p.plan_count + 8;
     p.plan_claim = p.plan_off + 8;
+    p.plan_done = p.plan_claim + 8;
+    if (mode != kPrefillRunOnly) {              // the work list is rewritten: earlier plans are void
+        ++ctx->plan_gen;
+        ctx->plan_valid = mode == kPrefillPlanOnly;
+        ctx->plan_key = key;
+        if (plan_out) *plan_out = ctx->plan_gen;
+    }
+    if (empty) return ok(ctx);
     // Large packs run as persistent workgroups over a device-built work list;
-    // small ones launch one workgroup per work unit (no planning launch).
+    // small ones launch one workgroup per work unit (no list to build).
     const int64_t est_units = ((int64_t)total_tokens * n_heads_q / 128) + 1;
     const bool persistent = est_units >= 8LL * ctx->num_cus && num_seqs <= slm::kPrefillPlanMaxSeqs;
+    const int phases = mode == kPrefillFull ? slm::kPrefillPlan | slm::kPrefillRun
+                                            : (mode == kPrefillPlanOnly ? slm::kPrefillPlan : slm::kPrefillRun);
     return SLM_LAUNCH(ctx, slm::launch_prefill_attn(p, head_dim, out_dtype == SLM_BF16, persistent, ctx->num_cus,
-                                                    ctx->launch_cache, ctx->stream), "prefill");
+                                                    ctx->launch_cache, ctx->stream, phases), "prefill");
+}
+
+}  // namespace
+
+slm_status slm_packed_prefill_attn(slm_ctx* ctx, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                                   int32_t max_seqlen, int32_t n_heads_q, int32_t n_heads_kv,
+                                   int32_t head_dim, float scale, void* out, slm_dtype out_dtype) {
+    return prefill_call(ctx, kPrefillFull, 0, nullptr, q, k, v, cu_seqlens, num_seqs, total_tokens, max_seqlen,
+                        n_heads_q, n_heads_kv, head_dim, scale, out, out_dtype);
+}
+
+slm_status slm_prefill_plan(slm_ctx* ctx, const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                            int32_t max_seqlen, int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                            uint64_t* plan) {
+    return prefill_call(ctx, kPrefillPlanOnly, 0, plan, nullptr, nullptr, nullptr, cu_seqlens, num_seqs,
+                        total_tokens, max_seqlen, n_heads_q, n_heads_kv, head_dim, 1.f, nullptr, SLM_F32);
+}
+
+slm_status slm_packed_prefill_attn_planned(slm_ctx* ctx, uint64_t plan, const uint16_t* q, const uint16_t* k,
+                                           const uint16_t* v, const int32_t* cu_seqlens, int32_t num_seqs,
+                                           int32_t total_tokens, int32_t max_seqlen, int32_t n_heads_q,
+                                           int32_t n_heads_kv, int32_t head_dim, float scale, void* out,
+                                           slm_dtype out_dtype) {
+    return prefill_call(ctx, kPrefillRunOnly, plan, nullptr, q, k, v, cu_seqlens, num_seqs, total_tokens,
+                        max_seqlen, n_heads_q, n_heads_kv, head_dim, scale, out, out_dtype);
 }
 
 slm_status slm_gather_last(slm_ctx* ctx, const void* hidden, const int32_t* cu_seqlens, int32_t num_seqs,

@@ -40,9 +40,10 @@
 extern "C" {
 #endif
 
-#define SLM_ABI_VERSION 5   /* 3: slm_beam_attn_args gained prompt_cu, prompt_rows;
+#define SLM_ABI_VERSION 6   /* 3: slm_beam_attn_args gained prompt_cu, prompt_rows;
                                4: slm_beam_backtrack, slm_beam_search;
-                               5: slm_packed_prefill_attn_noalloc */
+                               5: slm_packed_prefill_attn_noalloc;
+                               6: slm_prefill_plan, slm_packed_prefill_attn_planned */
 
 typedef enum {
     SLM_OK = 0,
@@ -111,6 +112,39 @@ slm_status slm_packed_prefill_attn(slm_ctx *ctx, const uint16_t *q, const uint16
                                    int32_t max_seqlen, int32_t n_heads_q,
                                    int32_t n_heads_kv, int32_t head_dim, float scale,
                                    void *out, slm_dtype out_dtype);
+
+/*
+ * The same attention with its work list built once per pack (abstract:
+ * Packed Prefill; the layers of one forward pass all run over the same
+ * packed batch, so the schedule of that batch is computed once).
+ *
+ * slm_prefill_plan builds, on the context's stream, the work list of the
+ * pack described by cu_seqlens and the sizes (the arguments of
+ * slm_packed_prefill_attn without the tensors) in the context's workspace,
+ * and returns its id in *plan.  A context holds one plan: any later
+ * slm_prefill_plan or slm_packed_prefill_attn call on it replaces the plan.
+ * Small packs, which run without a work list, get a plan id too.
+ *
+ * slm_packed_prefill_attn_planned computes exactly what
+ * slm_packed_prefill_attn computes for the same arguments, over the plan
+ * `plan` instead of a newly built list.  cu_seqlens (the same pointer,
+ * whose contents the caller keeps unchanged) and every size must be those
+ * the plan was built for, and the plan must still be the context's current
+ * one; otherwise SLM_ERR_INVALID_ARG and nothing is launched.  Runs over one
+ * plan may follow each other without limit (each run leaves the list's
+ * counters as the plan left them); they are ordered on the context's stream
+ * like every call, so they may also be captured in a graph and replayed.
+ */
+slm_status slm_prefill_plan(slm_ctx *ctx, const int32_t *cu_seqlens, int32_t num_seqs,
+                            int32_t total_tokens, int32_t max_seqlen, int32_t n_heads_q,
+                            int32_t n_heads_kv, int32_t head_dim, uint64_t *plan);
+slm_status slm_packed_prefill_attn_planned(slm_ctx *ctx, uint64_t plan, const uint16_t *q,
+                                           const uint16_t *k, const uint16_t *v,
+                                           const int32_t *cu_seqlens, int32_t num_seqs,
+                                           int32_t total_tokens, int32_t max_seqlen,
+                                           int32_t n_heads_q, int32_t n_heads_kv,
+                                           int32_t head_dim, float scale, void *out,
+                                           slm_dtype out_dtype);
 
 /*
  * Last-valid-token gather (§1.1: prefill-only outputs come from each

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert declared == set(slm.EXPORTED)
-    assert slm.abi_version() == 5
+    assert slm.abi_version() == 6
 
 
 @pytest.fixture
@@ -69,6 +69,49 @@ def test_prefill_validation(dry):
     e = _bf(0, 4, 64)
     assert _status(lambda: dry.packed_prefill_attn(e, _bf(0, 2, 64), _bf(0, 2, 64),
                                                    torch.zeros(1, dtype=torch.int32), 0)) == slm.SLM_OK
+
+
+def test_prefill_plan_validation(dry):
+    """A plan id is good for runs over the same cu_seqlens and sizes until
+    another prefill call on the context rebuilds the work list."""
+    q, k, v = _bf(10, 4, 64), _bf(10, 2, 64), _bf(10, 2, 64)
+    cu = torch.tensor([0, 3, 10], dtype=torch.int32)
+    plan = dry.prefill_plan(cu, 7, 10, 4, 2, 64)
+    for _ in range(3):
+        assert _status(lambda: dry.packed_prefill_attn_planned(plan, q, k, v, cu, 7)) == slm.SLM_OK
+    assert _status(lambda: dry.packed_prefill_attn_planned(plan, q, k, v, cu, 7, out_dtype=torch.bfloat16)) \
+        == slm.SLM_OK
+    # another pack (pointer), other sizes, an unknown id
+    cu2 = cu.clone()
+    assert _status(lambda: dry.packed_prefill_attn_planned(plan, q, k, v, cu2, 7)) == slm.SLM_ERR_INVALID_ARG
+    assert _status(lambda: dry.packed_prefill_attn_planned(plan, q, k, v, cu, 8)) == slm.SLM_ERR_INVALID_ARG
+    assert _status(lambda: dry.packed_prefill_attn_planned(plan, _bf(10, 2, 64), k, v, cu, 7)) \
+        == slm.SLM_ERR_INVALID_ARG
+    assert _status(lambda: dry.packed_prefill_attn_planned(plan + 1, q, k, v, cu, 7)) == slm.SLM_ERR_INVALID_ARG
+    # a plan's run checks its tensors like the plain call
+    big = torch.zeros(10 * 4 * 64 * 2, dtype=torch.bfloat16)
+    qa, oa = big[:2560].view(10, 4, 64), big[1280:1280 + 2560].view(10, 4, 64)
+    assert _status(lambda: dry.packed_prefill_attn_planned(plan, qa, k, v, cu, 7, out=oa, out_dtype=torch.bfloat16)) \
+        == slm.SLM_ERR_ALIAS
+    # a plain call or a new plan replaces it
+    assert _status(lambda: dry.packed_prefill_attn(q, k, v, cu, 7)) == slm.SLM_OK
+    assert _status(lambda: dry.packed_prefill_attn_planned(plan, q, k, v, cu, 7)) == slm.SLM_ERR_INVALID_ARG
+    plan2 = dry.prefill_plan(cu, 7, 10, 4, 2, 64)
+    assert plan2 != plan
+    plan3 = dry.prefill_plan(cu, 7, 10, 4, 2, 64)
+    assert _status(lambda: dry.packed_prefill_attn_planned(plan2, q, k, v, cu, 7)) == slm.SLM_ERR_INVALID_ARG
+    assert _status(lambda: dry.packed_prefill_attn_planned(plan3, q, k, v, cu, 7)) == slm.SLM_OK
+    # the plan call validates the pack like the plain call
+    assert _status(lambda: dry.prefill_plan(cu, 11, 10, 4, 2, 64)) == slm.SLM_ERR_INVALID_ARG   # max_seqlen > T
+    assert _status(lambda: dry.prefill_plan(cu, 7, 10, 3, 2, 64)) == slm.SLM_ERR_INVALID_ARG    # Hq % Hkv
+    assert _status(lambda: dry.prefill_plan(cu, 7, 10, 4, 2, 96)) == slm.SLM_ERR_UNSUPPORTED
+    small = slm.Context(device=-1, max_tokens=8)
+    assert _status(lambda: small.prefill_plan(cu, 7, 10, 4, 2, 64)) == slm.SLM_ERR_CAPACITY
+    # an empty pack plans and runs as a no-op
+    z = torch.zeros(1, dtype=torch.int32)
+    pe = dry.prefill_plan(z, 0, 0, 4, 2, 64)
+    assert _status(lambda: dry.packed_prefill_attn_planned(pe, _bf(0, 4, 64), _bf(0, 2, 64), _bf(0, 2, 64), z, 0)) \
+        == slm.SLM_OK
 
 
 def test_topk_validation(dry):

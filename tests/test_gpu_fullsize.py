@@ -4,7 +4,8 @@ host:
 
 * the 960-sequence prefill pack (T = 269,924, Hq16/Hkv8/D128): the whole
   output tensor of layer 0 within tolerance, and all 28 layer launches (one
-  Q/K/V set, as the bench runs them) bitwise equal;
+  Q/K/V set), both as plain calls and as runs over one plan (as the bench
+  runs them), bitwise equal;
 * the two fixed-step beam searches (32 requests x 100 beams, prompt 128, 4
   steps; 8 requests x 400 beams, prompt 480, 5 steps; 24 layers, vocabulary
   151,936) end to end through the one-call driver: every merge's tokens,
@@ -29,7 +30,7 @@ pytestmark = pytest.mark.gpu
 def test_prefill_throughput_whole_tensor_and_layer_launches(gpu):
     shape = wl.PREFILL_THROUGHPUT
     T, Hq, Hkv, D = shape.total_tokens, shape.n_heads_q, shape.n_heads_kv, shape.head_dim
-    note("prefill %s: 28 launches bitwise, whole layer-0 tensor vs the oracle (T=%d)" % (shape.name, T))
+    note("prefill %s: 28 plain + 28 planned launches bitwise, whole layer-0 tensor vs the oracle (T=%d)" % (shape.name, T))
     q = wl.torch_normal_bf16((T, Hq, D), (shape.base_seed, wl.TID_Q, 0, 0), "cuda")
     k = wl.torch_normal_bf16((T, Hkv, D), (shape.base_seed, wl.TID_K, 0, 0), "cuda")
     v = wl.torch_normal_bf16((T, Hkv, D), (shape.base_seed, wl.TID_V, 0, 0), "cuda")
@@ -41,6 +42,11 @@ def test_prefill_throughput_whole_tensor_and_layer_launches(gpu):
         out.fill_(float("nan"))                 # every launch must rewrite every element
         gpu.packed_prefill_attn(q, k, v, cu_d, shape.max_seqlen, out=out)
         assert torch.equal(out.view(torch.int32), out0.view(torch.int32)), "launch %d differs from launch 0" % layer
+    plan = gpu.prefill_plan(cu_d, shape.max_seqlen, T, Hq, Hkv, D)
+    for layer in range(shape.n_layers):
+        out.fill_(float("nan"))
+        gpu.packed_prefill_attn_planned(plan, q, k, v, cu_d, shape.max_seqlen, out=out)
+        assert torch.equal(out.view(torch.int32), out0.view(torch.int32)), "planned launch %d differs" % layer
     gpu.check()
     del out
     ref = oracle.prefill_attn(host_bits(q), host_bits(k), host_bits(v), cu)
