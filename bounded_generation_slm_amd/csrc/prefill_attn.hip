@@ -14,21 +14,26 @@
 // and row sum are in-lane plus one cross-half exchange, and the accumulator
 // layout of S^T is exactly the B-operand layout P^T needs: no shuffle of P.
 //
-// K/V staging: 32-key tiles go from HBM straight into a 3-stage LDS ring with
-// global_load_lds_dwordx4 (no register staging), two tiles ahead of the
-// compute, one workgroup barrier per tile.  K rows are stored with their
-// 16-byte chunks XOR-swizzled by row so the K operand reads are conflict-free.
-// V stays row-major; its V^T operand comes from ds_read_b64_tr_b16, whose
-// 16-lane transpose hands each lane one d column of four keys.
+// K/V staging: 32-key tiles go from HBM straight into LDS with
+// global_load_lds_dwordx4 (no register staging).  K rows are stored with
+// their 16-byte chunks XOR-swizzled by row so the K operand reads are
+// conflict-free.  V stays row-major; its V^T operand comes from
+// ds_read_b64_tr_b16, whose 16-lane transpose hands each lane one d column of
+// four keys.
 //
 // Two launch forms share the per-tile code:
-//   * one workgroup per work unit (small packs), XCD-aware block order;
+//   * one workgroup per work unit (small packs), XCD-aware block order, a
+//     3-stage ring two tiles ahead of the compute, one barrier per tile;
 //   * for large packs, a plan kernel lists the non-empty work units per XCD
 //     (the units of one (sequence, head block) on one XCD so they share its
 //     L2, heavier query tiles first), and persistent workgroups walk their
-//     XCD's list as one continuous K/V tile stream: the next unit's first
-//     tiles and its Q rows are in flight while the current unit finishes,
-//     and each unit's output leaves through unconditional buffer stores.
+//     XCD's list as one continuous K/V stream of 64-key steps (two tiles per
+//     barrier, a four-tile ring used as two halves): the next unit's first
+//     tiles are in flight while the current unit finishes, and each unit's
+//     output leaves through unconditional buffer stores.  The list depends
+//     only on cu_seqlens and the sizes, so it can be built once per pack and
+//     run by every layer (the plan and run phases); each run's last
+//     workgroup per XCD leaves the list's counters as the plan left them.
 #include <type_traits>
 
 #include "attn_tile.h"
