@@ -110,17 +110,36 @@ def test_decode(h, p, v, d, od):
         assert not ok
 
 
+def _host_array(n, fill):
+    """A host array of n device addresses (the per-step pointer arrays are
+    read on the host, so they must be real host memory of the documented
+    length; the addresses in them are never dereferenced on a dry run)."""
+    arr = (ctypes.c_void_p * max(n, 1))(*([fill or None] * max(n, 1)))
+    return arr, ctypes.cast(arr, ctypes.c_void_p).value
+
+
 @SETTINGS
-@given(p=st.lists(ptrs, min_size=20, max_size=20), v=st.lists(small, min_size=10, max_size=10), od=dtypes)
-def test_beam_search(h, p, v, od):
+@given(p=st.lists(ptrs, min_size=20, max_size=20), v=st.lists(small, min_size=10, max_size=10), od=dtypes,
+       present=st.lists(st.booleans(), min_size=5, max_size=5))
+def test_beam_search(h, p, v, od, present):
     a = slm._BeamSearchArgs()
     (a.n_layers, a.num_requests, a.width, a.prompt_len, a.n_steps, a.suffix_cap, a.n_heads_q, a.n_heads_kv,
      a.head_dim, a.vocab) = v
     a.scale, a.out_dtype = 0.125, od
     a.prefix_k, a.prefix_v, a.prompt_cu = (x or None for x in p[0:3])
-    a.cum0, a.logprobs, a.q, a.k_new, a.v_new = (x or None for x in p[3:8])
+    a.cum0 = p[3] or None
+    keep = []                                   # host arrays: logprobs has n_steps + 1 entries, the rest n_steps
+    for name, n, fill, there in zip(("logprobs", "q", "k_new", "v_new"), (v[4] + 1, v[4], v[4], v[4]), p[4:8],
+                                    present):
+        if there:
+            arr, addr = _host_array(n, fill)
+            keep.append(arr)
+            setattr(a, name, addr)
     a.suffix_k[0], a.suffix_k[1], a.suffix_v[0], a.suffix_v[1] = (x or None for x in p[8:12])
-    a.final_k, a.final_v, a.attn_out = (x or None for x in p[12:15])
+    a.final_k, a.final_v = (x or None for x in p[12:14])
+    if present[4]:
+        arr, a.attn_out = _host_array(v[4], p[14])
+        keep.append(arr)
     a.tokens, a.parent, a.cum, a.sequences = (x or None for x in p[15:19])
     a.prompt_rows = p[19] % 100
     ok = _ok(L.slm_beam_search(h, ctypes.byref(a)))
