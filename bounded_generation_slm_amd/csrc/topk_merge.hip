@@ -305,11 +305,12 @@ constexpr int kWDepth = 4;                          // the merge on logits: roun
 constexpr int kWBins = 256;
 
 // LDS layout of one wave, in 8-byte words: buf[soft + kWRound], hist[kWBins]
-// ints.  Widths above 256 get no first-round bound and would compact every
-// round or two while their own threshold is still loose, so their buffer
-// keeps a round's worth of slots (512) free after a compaction; narrower
-// ones compact at 512 keys, which raises their threshold sooner.  Four
-// workgroups fit a CU up to W = 256, three up to W = 512.
+// ints.  Above W = 256 a round's own W-th key is a loose bound (W of its 512
+// candidates are above it) and such a wave would compact every round or two
+// while its threshold is still loose, so its buffer keeps a round's worth of
+// slots (512) free after a compaction; narrower ones compact at 512 keys,
+// which raises their threshold sooner.  Four workgroups fit a CU up to
+// W = 256, three up to W = 512.
 __host__ __device__ inline int wave_soft_cap(int W) { return wide_width(W) ? W + kWRound : kWRound; }
 __host__ __device__ inline int wave_lds_words(int W) {
     return wave_soft_cap(W) + kWRound + kWBins / 2;
@@ -353,8 +354,12 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 }
 
 // k-th largest (1-based) of buf[0..cnt), wave-level radix select over the
-// live [min, max] range (see select_kth).
-__device__ uint64_t wave_select_kth(const uint64_t* buf, int* hist, int cnt, int k, int lane, int* err) {
+// live [min, max] range (see select_kth).  With k2 > 0, *b2 also receives,
+// from the first pass's histogram, a value below which at most cnt - k2 keys
+// lie (the lower edge of the bin holding the k2-th largest, minus one): at
+// least k2 keys are above it.
+__device__ uint64_t wave_select_kth(const uint64_t* buf, int* hist, int cnt, int k, int lane, int* err, int k2 = 0,
+                                    uint64_t* b2 = nullptr) {
     uint64_t lo = 0ull, hi = ~0ull;
     int c = cnt;
     for (int pass = 0;; ++pass) {
@@ -393,7 +398,7 @@ __device__ uint64_t wave_select_kth(const uint64_t* buf, int* hist, int cnt, int
         }
         wave_fence();
         const int incl = wave_incl_scan(sum, lane);
-        int above = incl - sum, digit = -1, dabove = 0, dcnt = 0;
+        int above = incl - sum, digit = -1, dabove = 0, dcnt = 0, digit2 = -1;
 #pragma unroll
         for (int j = 0; j < kWBins / kWLanes; ++j) {
             if (h[j] > 0 && above < k && k <= above + h[j]) {
@@ -401,7 +406,15 @@ __device__ uint64_t wave_select_kth(const uint64_t* buf, int* hist, int cnt, int
                 dabove = above;
                 dcnt = h[j];
             }
+            if (h[j] > 0 && above < k2 && k2 <= above + h[j]) digit2 = kWBins - 1 - (lane * (kWBins / kWLanes) + j);
             above += h[j];
+        }
+        if (pass == 0 && k2 > 0) {                  // the first pass's histogram covers every key
+            const uint64_t w2 = __ballot(digit2 >= 0);
+            if (w2) {
+                const uint64_t e2 = lo + ((uint64_t)__shfl(digit2, __builtin_ctzll(w2)) << shift);
+                *b2 = e2 > 0 ? e2 - 1ull : 0ull;
+            }
         }
         const uint64_t who = __ballot(digit >= 0);  // exactly one lane
         const int src = __builtin_ctzll(who);
@@ -419,8 +432,9 @@ __device__ uint64_t wave_select_kth(const uint64_t* buf, int* hist, int cnt, int
 // W-th key (the new threshold); cnt becomes W.  In place: a kept key moves
 // to pos + (kept lanes below it) <= its own index, and each group of 64 is
 // read before any of its writes, so no key is overwritten before it is read.
-__device__ uint64_t wave_compact(uint64_t* buf, int* hist, int& cnt, int W, int lane, int* err) {
-    const uint64_t kth = wave_select_kth(buf, hist, cnt, W, lane, err);
+__device__ uint64_t wave_compact(uint64_t* buf, int* hist, int& cnt, int W, int lane, int* err, int k2 = 0,
+                             uint64_t* b2 = nullptr) {
+    const uint64_t kth = wave_select_kth(buf, hist, cnt, W, lane, err, k2, b2);
     int pos = 0;
     for (int i0 = 0; i0 < cnt; i0 += kWLanes) {
         const int i = i0 + lane;
@@ -543,13 +557,15 @@ __global__ __launch_bounds__(kTkThreads, (DEPTH == stream_depth(false) ? 4 : 3))
     // and the q-th of them.
     auto shrink = [&]() {
         wave_fence();
-        const uint64_t own = wave_compact(buf, hist, cnt, W, lane, p.err);
+        uint64_t oq = 0;                                        // q keys above it: from the same select
+        const uint64_t own = wave_compact(buf, hist, cnt, W, lane, p.err, q < W ? q : 0, &oq);
         thr = own > thr ? own : thr;
-        const uint64_t oq = q < W ? wave_select_kth(buf, hist, W, q, lane, p.err) : own;
+        if (q >= W) oq = own;
         wave_fence();
         publish(own, oq);
     };
-    // Append the keys not below request r's shared threshold to its list.
+    // Append the keys not below request r's shared threshold, nor below this
+    // wave's own threshold (also a bound of r's W-th key), to r's list.
     auto count_keep = [&](uint64_t gu) {
         int k = 0;
         for (int i0 = 0; i0 < cnt; i0 += kWLanes) {
@@ -561,6 +577,7 @@ __global__ __launch_bounds__(kTkThreads, (DEPTH == stream_depth(false) ? 4 : 3))
     auto flush = [&]() {
         wave_fence();
         uint64_t gu = bound_take(bound_issue(p, r, lane, m_slots), lane, m_slots);
+        gu = thr > gu ? thr : gu;
         int n_keep = count_keep(gu);
         if (n_keep > W) {                                       // at most W keys per flush (list capacity)
             shrink();
@@ -621,7 +638,7 @@ __global__ __launch_bounds__(kTkThreads, (DEPTH == stream_depth(false) ? 4 : 3))
             for (int j = 0; j < NV; ++j)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sc[j * 4 + e] = c + src[j][e];   // the candidate score: one fp32 add
-            if (rd == 0 && W <= kWRound / 2) {                  // a piece's first round: bound it at once
+            if (rd == 0) {                                      // a piece's first round: bound it at once
                 bool valid[kWPerLane];
 #pragma unroll
                 for (int j = 0; j < NV; ++j)
@@ -655,7 +672,11 @@ __global__ __launch_bounds__(kTkThreads, (DEPTH == stream_depth(false) ? 4 : 3))
         // DEPTH rounds of loads stay in flight: before round rd + j the loads
         // of round rd + j + DEPTH - 1 go out into the buffer round rd + j - 1
         // freed.  The shared bound is read once per group of DEPTH rounds,
-        // issued with the group's first loads and taken up at its last round.
+        // issued with the group's first loads and taken up at its last round;
+        // in a piece's first group it is also read right after round 0 (whose
+        // W-th and q-th bounds every wave publishes at about the same time)
+        // and taken at rounds 1 and 3, so the waves start filtering on each
+        // other's first rounds instead of their own loose thresholds.
         // (Each step is its own instantiation, so every buffer index is a
         // constant and the buffers stay in registers.)
         uint64_t sh = 0;
@@ -664,15 +685,24 @@ __global__ __launch_bounds__(kTkThreads, (DEPTH == stream_depth(false) ? 4 : 3))
             constexpr int j = decltype(jc)::value;
             if constexpr (j == 0) {
                 fetch(rd + DEPTH - 1, B[DEPTH - 1]);
-                sh = load_relaxed(baddr);
+                if (rd != 0) sh = load_relaxed(baddr);
             } else {
                 fetch(rd + DEPTH - 1 + j, B[j - 1]);
+            }
+            if constexpr (j == 1 || (j == 3 && DEPTH > 4)) {
+                if (rd == 0) {                                  // a piece's first group: take the bound early
+                    const uint64_t u = bound_take(sh, lane, m_slots);
+                    thr = u > thr ? u : thr;
+                    sh = load_relaxed(baddr);
+                }
             }
             if constexpr (j == DEPTH - 1) {
                 const uint64_t u = bound_take(sh, lane, m_slots);
                 thr = u > thr ? u : thr;
             }
             round(rd + j, B[j]);
+            if constexpr (j == 0)
+                if (rd == 0) sh = load_relaxed(baddr);          // after this round's own bounds went out
             return rd + j + 1 < rounds;                         // wave-uniform
         };
         for_each_step<DEPTH - 1>([&](auto jc) __attribute__((always_inline)) {
