@@ -239,23 +239,27 @@ __device__ __forceinline__ void insert(SelectorLds& s, const uint64_t (&keys)[kP
 }
 
 // The W kept keys s.buf[0..n) in descending order, with no sort: keys are
-// distinct, so a key's position is the number of kept keys above it (one
-// pass of LDS broadcast reads per key, no barrier).  out(pos, key) for every
-// pos < W; positions n..W-1 (fewer than W keys) get key 0, which ranks below
-// every key.  s.buf must be final (after a barrier).
+// distinct, so a key's position is the number of kept keys above it.  Each
+// thread ranks its keys j and j + 256 (W <= 512) in one pass over the kept
+// keys, read two at a time (a zero after the last ranks below every key).
+// out(pos, key) for every pos < W; positions n..W-1 (fewer than W keys) get
+// key 0, which ranks below every key.  s.buf must be final (after a
+// barrier); all threads call it.
 template <class F>
-__device__ __forceinline__ void write_ranked(const SelectorLds& s, int n, int W, F&& out) {
-    for (int j = threadIdx.x; j < W; j += kTkThreads) {
-        if (j >= n) {
-            out(j, 0ull);
-            continue;
-        }
-        const uint64_t key = s.buf[j];
-        int pos = 0;
-#pragma unroll 8
-        for (int i = 0; i < n; ++i) pos += s.buf[i] > key ? 1 : 0;
-        out(pos, key);
+__device__ __forceinline__ void write_ranked(SelectorLds& s, int n, int W, F&& out) {
+    if (threadIdx.x == 0) s.buf[n] = 0ull;          // n <= W <= kMaxW: inside the buffer
+    __syncthreads();
+    const int j0 = threadIdx.x, j1 = threadIdx.x + kTkThreads;
+    const uint64_t k0 = j0 < n ? s.buf[j0] : ~0ull, k1 = j1 < n ? s.buf[j1] : ~0ull;
+    int p0 = 0, p1 = 0;
+#pragma unroll 4
+    for (int i = 0; i < n; i += 2) {
+        const uint64_t a = s.buf[i], b = s.buf[i + 1];
+        p0 += (a > k0 ? 1 : 0) + (b > k0 ? 1 : 0);
+        p1 += (a > k1 ? 1 : 0) + (b > k1 ? 1 : 0);
     }
+    if (j0 < W) out(j0 < n ? p0 : j0, j0 < n ? k0 : 0ull);
+    if (j1 < W) out(j1 < n ? p1 : j1, j1 < n ? k1 : 0ull);
 }
 
 __device__ __forceinline__ uint64_t load_relaxed(const uint64_t* p) {
@@ -729,17 +733,22 @@ __global__ __launch_bounds__(kTkThreads) void topk_stage2_kernel(const TopkParam
     }
     __syncthreads();
     const int rounds = (n + kRound - 1) / kRound;
-    for (int rd = 0; rd < rounds; ++rd) {
-        const uint64_t thr = s.thr;
-        uint64_t keys[kPerThread];
+    auto fetch = [&](int rd, uint64_t (&keys)[kPerThread]) {
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j) {
             const int i = rd * kRound + j * kTkThreads + threadIdx.x;
             keys[j] = i < n ? in[i] : 0ull;
         }
-        insert(s, keys, thr);
+    };
+    uint64_t cur[kPerThread], nxt[kPerThread];      // the next round's keys load during this round
+    fetch(0, cur);
+    for (int rd = 0; rd < rounds; ++rd) {
+        if (rd + 1 < rounds) fetch(rd + 1, nxt);
+        insert(s, cur, s.thr);
         __syncthreads();
         if (s.cnt > kSoftCap) compact(s, W, p.err);
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) cur[j] = nxt[j];
     }
     compact(s, W, p.err);
     write_ranked(s, min(s.cnt, W), W, [&](int j, uint64_t key) {
