@@ -148,6 +148,7 @@ struct TopkParams {
     uint64_t* req_state;                // workspace: [R] x kTopkStateWords (threshold, count), zero between calls
     int64_t list_cap;                   // keys per request list
     int64_t seg;                        // candidates per stage-1 wave (a multiple of 4)
+    int wpr, kslices;                   // sliced ranges: waves per request, slices per wave (0: contiguous)
     int num_requests, beams_in, vocab, width;
     // merge on logits only (logprobs then holds the logits):
     struct Piece {                      // one row's part of one stage-1 range
@@ -185,6 +186,10 @@ int beam_topk_blocks_per_cu(int width);     // resident stage-1 workgroups (4 wa
 constexpr int64_t kTopkMinSegment = 4096;
 constexpr int kTopkStateWords = 64;     // 512-byte state line per request
 constexpr int kTopkMaxChunks = 64;      // list slots per request at least
+// stage-1 slices per wave when a request's candidates are sliced over its
+// waves (each slice costs the stream pipeline one refill: 3 measured best
+// against 2, 4 and 8 at 151,936-token vocabularies)
+constexpr int kTopkSlices = 3;
 size_t beam_decode_lds_bytes(int head_dim, int prompt_len);
 constexpr int kTopkMaxWidth = 512;
 constexpr int kDecodeMaxSuffix = 8;     // hist_len + 1 <= 8

@@ -531,6 +531,17 @@ slm_status slm_beam_topk_merge(slm_ctx* ctx, const float* logprobs, const float*
     }
     const int64_t resident = (int64_t)ctx->num_cus * bpc * 4;
     p.seg = slm::beam_topk_segment(num_requests, beams_in, vocab, resident, ctx->topk_lists);
+    // sliced ranges where every slice still holds at least kTopkMinSegment
+    // candidates and the request's waves fit its list (one flush each)
+    {
+        const int k = slm::kTopkSlices;
+        const int64_t wpr = resident / num_requests / 4 * 4;
+        if (k > 0 && wpr >= 4 && wpr < ctx->topk_lists &&
+            (int64_t)beams_in * vocab / (wpr * k) >= slm::kTopkMinSegment) {
+            p.wpr = (int)wpr;
+            p.kslices = k;
+        }
+    }
     return SLM_LAUNCH(ctx, slm::launch_beam_topk_merge(p, ctx->stream), "topk");
 }
 

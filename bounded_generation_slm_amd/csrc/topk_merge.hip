@@ -15,12 +15,18 @@
 // unique set and every selection below is exact.
 //
 // Two stages:
-//   stage 1: the flattened candidates of the call are split into equal
-//            ranges, one per resident wave; a wave streams its range once,
-//            keeping its top W keys of each request against a threshold
-//            shared per request, and appends the keys not below that shared
-//            bound to the request's list.  Exact: every threshold is backed
-//            by W keys at or above it, so no final winner is dropped.
+//   stage 1: each request's candidates are split among an equal share of
+//            the resident waves, each wave taking kTopkSlices equal slices
+//            spread over the request (one from each group of slices, in
+//            alternating order, so a wave with an early, in a search
+//            higher-ranked and costlier, slice also gets a late one); where
+//            slices would be short, the flattened candidates of the call are
+//            split into equal contiguous ranges instead.  A wave streams its
+//            candidates once, keeping its top W keys of each request against
+//            a threshold shared per request, and appends the keys not below
+//            that shared bound to the request's list.  Exact: every
+//            threshold is backed by W keys at or above it, so no final
+//            winner is dropped.
 //   stage 2: one workgroup per request reads its list, keeps the top W and
 //            writes tokens, parents and scores in rank order.
 // The streaming selector keeps candidates above a running threshold in an
@@ -533,9 +539,27 @@ __global__ __launch_bounds__(kTkThreads, (DEPTH == stream_depth(false) ? 4 : 3))
     const int V = p.vocab, W = p.width;
     const int64_t req_len = (int64_t)p.beams_in * V;           // candidates of one request
     const int64_t total = (int64_t)p.num_requests * req_len;
-    int64_t a = wid * p.seg;                                    // this wave's range [a, end)
+    // This wave's candidates: one contiguous range of p.seg, or (sliced) k of
+    // the wpr * k equal slices of request w / wpr, one from each group of wpr
+    // consecutive slices (l = w % wpr picks which), so every wave streams the
+    // same amount and each stretch of rows is spread over many waves.  Slice bounds are
+    // multiples of 4 (whole 16-byte loads), the last one the request's end.
+    const bool sliced = p.kslices > 0;
+    const int64_t den = sliced ? (int64_t)p.wpr * p.kslices : 1;
+    const int64_t wl = sliced ? wid % p.wpr : 0;
+    const int64_t rbase = sliced ? wid / p.wpr * req_len : 0;
+    auto slice_at = [&](int64_t j) {
+        return rbase + (j == den ? req_len : (j * req_len / den) & ~(int64_t)3);
+    };
+    // pass si takes slice si * wpr + l on even passes and the mirrored
+    // (si + 1) * wpr - 1 - l on odd ones, so a wave with an early (in a
+    // search: higher-ranked, heavier) slice also gets a late one
+    auto slice_of = [&](int si) {
+        return (si & 1) ? (int64_t)(si + 1) * p.wpr - 1 - wl : (int64_t)si * p.wpr + wl;
+    };
+    int64_t a = sliced ? slice_at(slice_of(0)) : wid * p.seg;   // this wave's range [a, end)
     if (a >= total) return;                                     // no barriers below: waves are independent
-    const int64_t end = min(total, a + p.seg);
+    int64_t end = sliced ? slice_at(slice_of(0) + 1) : min(total, a + p.seg);
     uint64_t* buf = wave_lds + (size_t)wave * wave_lds_words(W);
     const int soft = wave_soft_cap(W);
     int* hist = (int*)(buf + soft + kWRound);
@@ -604,6 +628,7 @@ __global__ __launch_bounds__(kTkThreads, (DEPTH == stream_depth(false) ? 4 : 3))
     };
 
     constexpr int NV = kWPerLane / 4;
+    for (int si = 0;;) {
     while (a < end) {
         const int64_t row = a / V;                              // r * Win + b
         const int rr = (int)(row / p.beams_in);
@@ -716,6 +741,11 @@ __global__ __launch_bounds__(kTkThreads, (DEPTH == stream_depth(false) ? 4 : 3))
         for (; rd < rounds; rd += DEPTH)
             if (!for_each_step<DEPTH>(step)) break;
         a = pe;
+    }
+        if (!sliced || ++si == p.kslices) break;
+        const int64_t j = slice_of(si);
+        a = slice_at(j);
+        end = slice_at(j + 1);
     }
     flush();
 }
@@ -1122,7 +1152,7 @@ hipError_t launch_beam_topk_merge(const TopkParams& p, hipStream_t stream) {
     const bool vec = (p.vocab % 4 == 0) && (((uintptr_t)p.logprobs & 15) == 0);
     // stage 2 resets the shared state it consumed; nothing else touches it
     const int64_t total = (int64_t)p.num_requests * p.beams_in * p.vocab;
-    const int64_t waves = (total + p.seg - 1) / p.seg;
+    const int64_t waves = p.kslices > 0 ? (int64_t)p.num_requests * p.wpr : (total + p.seg - 1) / p.seg;
     const int64_t blocks = (waves + kTkThreads / kWLanes - 1) / (kTkThreads / kWLanes);
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const size_t lds = beam_topk_stage1_lds(p.width);

@@ -50,6 +50,18 @@ def test_topk_shapes_and_ties(gpu, R, Win, V, W):
     _eq(_topk(gpu, lpn, cum, W), oracle.topk_merge(lpn, cum, W), "normal")
 
 
+@pytest.mark.parametrize("R,Win,V,W", [(32, 16, 100003, 64), (8, 128, 65536, 300)])
+def test_topk_sliced_ranges(gpu, R, Win, V, W):
+    # large enough per request that each request's candidates are sliced over
+    # its waves (three slices each, at least 4,096 candidates a slice); an odd
+    # vocabulary takes the 4-byte load path; exact ties straddle slice bounds
+    note("topk sliced R=%d Win=%d V=%d W=%d" % (R, Win, V, W))
+    rng = np.random.default_rng(R * 7 + V)
+    lp = (np.round(rng.standard_normal((R, Win, V), dtype=np.float32) * 8) / 8 - 12).astype(np.float32)
+    cum = -np.sort(-(np.round(rng.standard_normal((R, Win)) * 4) / 4).astype(np.float32), axis=1)   # ranked beams
+    _eq(_topk(gpu, lp, cum, W), oracle.topk_merge(lp, cum, W), "sliced")
+
+
 def test_topk_negative_zero_equals_positive_zero(gpu):
     note("topk -0 vs +0 scores")
     lp = np.array([[[-0.0, 0.0, -1.0, 0.0]]], np.float32)
