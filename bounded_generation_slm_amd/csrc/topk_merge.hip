@@ -542,8 +542,9 @@ __global__ __launch_bounds__(kTkThreads, (DEPTH == stream_depth(false) ? 4 : 3))
     // This wave's candidates: one contiguous range of p.seg, or (sliced) k of
     // the wpr * k equal slices of request w / wpr, one from each group of wpr
     // consecutive slices (l = w % wpr picks which), so every wave streams the
-    // same amount and each stretch of rows is spread over many waves.  Slice bounds are
-    // multiples of 4 (whole 16-byte loads), the last one the request's end.
+    // same amount and each stretch of rows is spread over many waves.  Slice
+    // bounds are multiples of 4 (whole 16-byte loads), the last one the
+    // request's end.
     const bool sliced = p.kslices > 0;
     const int64_t den = sliced ? (int64_t)p.wpr * p.kslices : 1;
     const int64_t wl = sliced ? wid % p.wpr : 0;
@@ -629,119 +630,119 @@ __global__ __launch_bounds__(kTkThreads, (DEPTH == stream_depth(false) ? 4 : 3))
 
     constexpr int NV = kWPerLane / 4;
     for (int si = 0;;) {
-    while (a < end) {
-        const int64_t row = a / V;                              // r * Win + b
-        const int rr = (int)(row / p.beams_in);
-        if (rr != r) {                                          // the range enters the next request
-            flush();
-            r = rr;
-            thr = bound_take(bound_issue(p, r, lane, m_slots), lane, m_slots);
-            pub = 0;
-            pubq = 0;
-        }
-        const int64_t pe = min(end, (row + 1) * V);             // this piece: [a, pe) inside one row
-        const int n = (int)(pe - a);
-        const float* lp = p.logprobs + a;
-        const float c = p.cum[row];
-        const uint32_t f0 = (uint32_t)(a - (int64_t)r * req_len);   // flat index b*V + v of lp[0]
-        const uint64_t* baddr = bound_addr(p, r, lane, m_slots);
-        const int rounds = (n + kWRound - 1) / kWRound;
-        f32x4 B[DEPTH][NV];
-        // loads of round rd (clamped into the piece: rounds past its end
-        // re-read valid addresses, and their values are never used)
-        auto fetch = [&](int rd, f32x4 (&dst)[NV]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int j = 0; j < NV; ++j) {
-                const int i0 = rd * kWRound + (j * kWLanes + lane) * 4;
-                if (VEC) {
-                    dst[j] = stream_load16(lp + min(i0, n - 4));
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) dst[j][e] = stream_load4(lp + min(i0 + e, n - 1));
-                }
+        while (a < end) {
+            const int64_t row = a / V;                              // r * Win + b
+            const int rr = (int)(row / p.beams_in);
+            if (rr != r) {                                          // the range enters the next request
+                flush();
+                r = rr;
+                thr = bound_take(bound_issue(p, r, lane, m_slots), lane, m_slots);
+                pub = 0;
+                pubq = 0;
             }
-        };
-        auto round = [&](int rd, f32x4 (&src)[NV]) __attribute__((always_inline)) {
-            float sc[kWPerLane];
-#pragma unroll
-            for (int j = 0; j < NV; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sc[j * 4 + e] = c + src[j][e];   // the candidate score: one fp32 add
-            if (rd == 0) {                                      // a piece's first round: bound it at once
-                bool valid[kWPerLane];
-#pragma unroll
+            const int64_t pe = min(end, (row + 1) * V);             // this piece: [a, pe) inside one row
+            const int n = (int)(pe - a);
+            const float* lp = p.logprobs + a;
+            const float c = p.cum[row];
+            const uint32_t f0 = (uint32_t)(a - (int64_t)r * req_len);   // flat index b*V + v of lp[0]
+            const uint64_t* baddr = bound_addr(p, r, lane, m_slots);
+            const int rounds = (n + kWRound - 1) / kWRound;
+            f32x4 B[DEPTH][NV];
+            // loads of round rd (clamped into the piece: rounds past its end
+            // re-read valid addresses, and their values are never used)
+            auto fetch = [&](int rd, f32x4 (&dst)[NV]) __attribute__((always_inline)) {
+    #pragma unroll
+                for (int j = 0; j < NV; ++j) {
+                    const int i0 = rd * kWRound + (j * kWLanes + lane) * 4;
+                    if (VEC) {
+                        dst[j] = stream_load16(lp + min(i0, n - 4));
+                    } else {
+    #pragma unroll
+                        for (int e = 0; e < 4; ++e) dst[j][e] = stream_load4(lp + min(i0 + e, n - 1));
+                    }
+                }
+            };
+            auto round = [&](int rd, f32x4 (&src)[NV]) __attribute__((always_inline)) {
+                float sc[kWPerLane];
+    #pragma unroll
                 for (int j = 0; j < NV; ++j)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) valid[j * 4 + e] = (j * kWLanes + lane) * 4 + e < n;
-                const uint64_t rb = round_bound(sc, valid, W);
-                const uint64_t rq = q < W ? round_bound(sc, valid, q) : rb;
-                thr = rb > thr ? rb : thr;
-                publish(rb, rq);
-            }
-            const float ts = thr_score(thr);
-            bool maybe = false;
-#pragma unroll
-            for (int k = 0; k < kWPerLane; ++k) maybe |= sc[k] >= ts;
-            if (__ballot(maybe) == 0) return;                   // the common case once a threshold is set
-#pragma unroll
-            for (int j = 0; j < NV; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool ok = sc[j * 4 + e] >= ts;
-                    if (__ballot(ok) == 0) continue;            // uniform: no lane has a candidate here
-                    const int i = rd * kWRound + (j * kWLanes + lane) * 4 + e;
-                    const uint64_t key = (ok && i < n) ? make_key(sc[j * 4 + e], f0 + (uint32_t)i) : 0ull;
-                    const bool pass = key > thr;
-                    const uint64_t m = __ballot(pass);
-                    if (pass) buf[cnt + lanes_below(m)] = key;
-                    cnt += __popcll(m);
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) sc[j * 4 + e] = c + src[j][e];   // the candidate score: one fp32 add
+                if (rd == 0) {                                      // a piece's first round: bound it at once
+                    bool valid[kWPerLane];
+    #pragma unroll
+                    for (int j = 0; j < NV; ++j)
+    #pragma unroll
+                        for (int e = 0; e < 4; ++e) valid[j * 4 + e] = (j * kWLanes + lane) * 4 + e < n;
+                    const uint64_t rb = round_bound(sc, valid, W);
+                    const uint64_t rq = q < W ? round_bound(sc, valid, q) : rb;
+                    thr = rb > thr ? rb : thr;
+                    publish(rb, rq);
                 }
-            if (cnt > soft) shrink();
-        };
-        // DEPTH rounds of loads stay in flight: before round rd + j the loads
-        // of round rd + j + DEPTH - 1 go out into the buffer round rd + j - 1
-        // freed.  The shared bound is read once per group of DEPTH rounds,
-        // issued with the group's first loads and taken up at its last round;
-        // in a piece's first group it is also read right after round 0 (whose
-        // W-th and q-th bounds every wave publishes at about the same time)
-        // and taken at rounds 1 and 3, so the waves start filtering on each
-        // other's first rounds instead of their own loose thresholds.
-        // (Each step is its own instantiation, so every buffer index is a
-        // constant and the buffers stay in registers.)
-        uint64_t sh = 0;
-        int rd = 0;
-        auto step = [&](auto jc) __attribute__((always_inline)) {   // false once the piece is done
-            constexpr int j = decltype(jc)::value;
-            if constexpr (j == 0) {
-                fetch(rd + DEPTH - 1, B[DEPTH - 1]);
-                if (rd != 0) sh = load_relaxed(baddr);
-            } else {
-                fetch(rd + DEPTH - 1 + j, B[j - 1]);
-            }
-            if constexpr (j == 1 || (j == 3 && DEPTH > 4)) {
-                if (rd == 0) {                                  // a piece's first group: take the bound early
+                const float ts = thr_score(thr);
+                bool maybe = false;
+    #pragma unroll
+                for (int k = 0; k < kWPerLane; ++k) maybe |= sc[k] >= ts;
+                if (__ballot(maybe) == 0) return;                   // the common case once a threshold is set
+    #pragma unroll
+                for (int j = 0; j < NV; ++j)
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bool ok = sc[j * 4 + e] >= ts;
+                        if (__ballot(ok) == 0) continue;            // uniform: no lane has a candidate here
+                        const int i = rd * kWRound + (j * kWLanes + lane) * 4 + e;
+                        const uint64_t key = (ok && i < n) ? make_key(sc[j * 4 + e], f0 + (uint32_t)i) : 0ull;
+                        const bool pass = key > thr;
+                        const uint64_t m = __ballot(pass);
+                        if (pass) buf[cnt + lanes_below(m)] = key;
+                        cnt += __popcll(m);
+                    }
+                if (cnt > soft) shrink();
+            };
+            // DEPTH rounds of loads stay in flight: before round rd + j the loads
+            // of round rd + j + DEPTH - 1 go out into the buffer round rd + j - 1
+            // freed.  The shared bound is read once per group of DEPTH rounds,
+            // issued with the group's first loads and taken up at its last round;
+            // in a piece's first group it is also read right after round 0 (whose
+            // W-th and q-th bounds every wave publishes at about the same time)
+            // and taken at rounds 1 and 3, so the waves start filtering on each
+            // other's first rounds instead of their own loose thresholds.
+            // (Each step is its own instantiation, so every buffer index is a
+            // constant and the buffers stay in registers.)
+            uint64_t sh = 0;
+            int rd = 0;
+            auto step = [&](auto jc) __attribute__((always_inline)) {   // false once the piece is done
+                constexpr int j = decltype(jc)::value;
+                if constexpr (j == 0) {
+                    fetch(rd + DEPTH - 1, B[DEPTH - 1]);
+                    if (rd != 0) sh = load_relaxed(baddr);
+                } else {
+                    fetch(rd + DEPTH - 1 + j, B[j - 1]);
+                }
+                if constexpr (j == 1 || (j == 3 && DEPTH > 4)) {
+                    if (rd == 0) {                                  // a piece's first group: take the bound early
+                        const uint64_t u = bound_take(sh, lane, m_slots);
+                        thr = u > thr ? u : thr;
+                        sh = load_relaxed(baddr);
+                    }
+                }
+                if constexpr (j == DEPTH - 1) {
                     const uint64_t u = bound_take(sh, lane, m_slots);
                     thr = u > thr ? u : thr;
-                    sh = load_relaxed(baddr);
                 }
-            }
-            if constexpr (j == DEPTH - 1) {
-                const uint64_t u = bound_take(sh, lane, m_slots);
-                thr = u > thr ? u : thr;
-            }
-            round(rd + j, B[j]);
-            if constexpr (j == 0)
-                if (rd == 0) sh = load_relaxed(baddr);          // after this round's own bounds went out
-            return rd + j + 1 < rounds;                         // wave-uniform
-        };
-        for_each_step<DEPTH - 1>([&](auto jc) __attribute__((always_inline)) {
-            fetch(decltype(jc)::value, B[decltype(jc)::value]);
-            return true;
-        });
-        for (; rd < rounds; rd += DEPTH)
-            if (!for_each_step<DEPTH>(step)) break;
-        a = pe;
-    }
+                round(rd + j, B[j]);
+                if constexpr (j == 0)
+                    if (rd == 0) sh = load_relaxed(baddr);          // after this round's own bounds went out
+                return rd + j + 1 < rounds;                         // wave-uniform
+            };
+            for_each_step<DEPTH - 1>([&](auto jc) __attribute__((always_inline)) {
+                fetch(decltype(jc)::value, B[decltype(jc)::value]);
+                return true;
+            });
+            for (; rd < rounds; rd += DEPTH)
+                if (!for_each_step<DEPTH>(step)) break;
+            a = pe;
+        }
         if (!sliced || ++si == p.kslices) break;
         const int64_t j = slice_of(si);
         a = slice_at(j);
