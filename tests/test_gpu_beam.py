@@ -50,7 +50,7 @@ def test_topk_shapes_and_ties(gpu, R, Win, V, W):
     _eq(_topk(gpu, lpn, cum, W), oracle.topk_merge(lpn, cum, W), "normal")
 
 
-@pytest.mark.parametrize("R,Win,V,W", [(32, 16, 100003, 64), (8, 128, 65536, 300)])
+@pytest.mark.parametrize("R,Win,V,W", [(32, 16, 100003, 64), (8, 128, 65536, 300), (64, 8, 100000, 300)])
 def test_topk_sliced_ranges(gpu, R, Win, V, W):
     # large enough per request that each request's candidates are sliced over
     # its waves (three slices each, at least 4,096 candidates a slice); an odd
