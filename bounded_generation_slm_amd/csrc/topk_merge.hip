@@ -24,7 +24,8 @@
 //            split into equal contiguous ranges instead.  A wave streams its
 //            candidates once, keeping its top W keys of each request against
 //            a threshold shared per request, and appends the keys not below
-//            that shared bound to the request's list.  Exact: every
+//            that shared bound (nor its own threshold) to the request's
+//            list.  Exact: every
 //            threshold is backed by W keys at or above it, so no final
 //            winner is dropped.
 //   stage 2: one workgroup per request reads its list, keeps the top W and
