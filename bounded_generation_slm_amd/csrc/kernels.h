@@ -179,10 +179,15 @@ int64_t beam_topk_logits_segment(int num_requests, int beams_in, int vocab, int6
                                  int64_t parts_cap, int& rpw, int& rows_per_chunk, int& chunks);
 int beam_topk_logits_blocks_per_cu(int width);
 // candidates per stage-1 wave: the call split evenly over the resident waves,
-// at least kTopkMinSegment, and few enough ranges per request for its list
+// at least kTopkMinRange, and few enough ranges per request for its list
 // (`lists` slots of W keys)
 int64_t beam_topk_segment(int num_requests, int beams_in, int vocab, int64_t resident_waves, int64_t lists);
 int beam_topk_blocks_per_cu(int width);     // resident stage-1 workgroups (4 waves) per CU
+// Shortest stage-1 range of the merge on log-probs (first merges, one beam
+// per request, measured best at 2,048: 1,024 tied at 8 x 400 beams and ran
+// 4% slower at 32 x 100, 4,096 ran 10-35% slower)
+constexpr int64_t kTopkMinRange = 2048;
+// shortest sliced range, and shortest range of the merge on logits
 constexpr int64_t kTopkMinSegment = 4096;
 constexpr int kTopkStateWords = 64;     // 512-byte state line per request
 constexpr int kTopkMaxChunks = 64;      // list slots per request at least

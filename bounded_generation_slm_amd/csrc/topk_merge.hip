@@ -1142,7 +1142,7 @@ int64_t beam_topk_segment(int num_requests, int beams_in, int vocab, int64_t res
     const int64_t total = (int64_t)num_requests * beams_in * vocab;
     const int64_t req_len = (int64_t)beams_in * vocab;
     int64_t seg = (total + resident_waves - 1) / std::max<int64_t>(1, resident_waves);   // one range per resident wave
-    seg = std::max<int64_t>(seg, kTopkMinSegment);
+    seg = std::max<int64_t>(seg, kTopkMinRange);
     // a request's list takes at most W keys from each range that overlaps it:
     // ceil(req_len / seg) + 1 ranges must fit its `lists` W-key slots
     seg = std::max<int64_t>(seg, (req_len + lists - 2) / std::max<int64_t>(1, lists - 1));
