@@ -525,6 +525,18 @@ __device__ __forceinline__ bool for_each_step(F&& f) {
     return for_each_step_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Issue priority of the calling wave (s_setprio takes an immediate; k is
+// wave-uniform).
+__device__ __forceinline__ void set_wave_prio(int k) {
+    if (k == 0)
+        __builtin_amdgcn_s_setprio(0);
+    else if (k == 1)
+        __builtin_amdgcn_s_setprio(1);
+    else if (k == 2)
+        __builtin_amdgcn_s_setprio(2);
+    else
+        __builtin_amdgcn_s_setprio(3);
+}
 __device__ __forceinline__ f32x4 stream_load16(const float* p) {
     return __builtin_nontemporal_load((const f32x4*)p);
 }
@@ -630,6 +642,15 @@ __global__ __launch_bounds__(kTkThreads, (DEPTH == stream_depth(false) ? 4 : 3))
     };
 
     constexpr int NV = kWPerLane / 4;
+    // Wide widths run three workgroups per CU, and under oldest-first issue
+    // arbitration the workgroups dispatched later to a CU streamed ~15% slower,
+    // so the call ended with them.  There each wave steps its issue priority
+    // through the four levels, one per group of DEPTH rounds, starting from its
+    // index mod 4, so no wave stays behind the others for long.  (At four
+    // workgroups per CU the rotation measured slightly slower; those keep the
+    // default priority.)
+    constexpr bool rotate = DEPTH > stream_depth(false);
+    int prio = (int)(wid & 3);
     for (int si = 0;;) {
         while (a < end) {
             const int64_t row = a / V;                              // r * Win + b
@@ -740,8 +761,10 @@ __global__ __launch_bounds__(kTkThreads, (DEPTH == stream_depth(false) ? 4 : 3))
                 fetch(decltype(jc)::value, B[decltype(jc)::value]);
                 return true;
             });
-            for (; rd < rounds; rd += DEPTH)
+            for (; rd < rounds; rd += DEPTH) {
+                if constexpr (rotate) set_wave_prio(prio++ & 3);
                 if (!for_each_step<DEPTH>(step)) break;
+            }
             a = pe;
         }
         if (!sliced || ++si == p.kslices) break;
