@@ -858,6 +858,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_logits_stage1_kernel(const To
     int* hist = (int*)(buf + soft + kWRound);
 
     constexpr int NV = BF16 ? 1 : kWPerLane / 4;               // 16-byte registers per round
+    // issue priority stepped through the four levels per group of rounds, as
+    // in the merge on log-probs (here it measured faster at every width)
+    int prio = (int)(wid & 3);
     // element k (0..7) of this lane in round rd
     auto elem = [&](int rd, int k) {
         return BF16 ? rd * kWRound + lane * 8 + k : rd * kWRound + ((k >> 2) * kWLanes + lane) * 4 + (k & 3);
@@ -961,6 +964,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_logits_stage1_kernel(const To
         fetch(1, B1);
         fetch(2, B2);
         for (int rd = 0; rd < rounds; rd += kWDepth) {
+            set_wave_prio(prio++ & 3);
             fetch(rd + 3, B3);
             round(rd, B0);
             if (rd + 1 >= rounds) break;
