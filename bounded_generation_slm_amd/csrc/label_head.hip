@@ -74,18 +74,21 @@ __global__ __launch_bounds__(kLhWaves * kWave) void label_logits_kernel(const La
     }
 }
 
-constexpr int kLhPerLane = kLabelMax / kWave;           // logits one lane holds
+constexpr int kLhPerLane = kLabelMax / kWave;           // logits one lane holds at most
 
+// PER: logits per lane, at least ceil(L / 64).  Every loop below is unrolled
+// over PER, so a variant sized for 4,096 labels spent ~20 us on 64.
+template <int PER>
 __global__ __launch_bounds__(kLhWaves * kWave) void label_select_kernel(const LabelHeadParams p) {
     const int lane = threadIdx.x & 63;
     const int b = blockIdx.x * kLhWaves + (threadIdx.x >> 6);
     if (b >= p.num_seqs) return;                        // whole waves: no barriers below
     const int L = p.num_labels;
     const float* zrow = p.logits + (int64_t)b * L;
-    float z[kLhPerLane];                                // label lane + 64 t
+    float z[PER];                                       // label lane + 64 t
     float m = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < kLhPerLane; ++t) {
+    for (int t = 0; t < PER; ++t) {
         const int j = lane + 64 * t;
         z[t] = j < L ? zrow[j] : -INFINITY;
         m = fmaxf(m, z[t]);
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(kLhWaves * kWave) void label_select_kernel(const La
     const float mc = m * kLog2eLh;
     float s = 0.f;
 #pragma unroll
-    for (int t = 0; t < kLhPerLane; ++t)
+    for (int t = 0; t < PER; ++t)
         if (lane + 64 * t < L) s += fast_exp2(fmaf(z[t], kLog2eLh, -mc));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(kLhWaves * kWave) void label_select_kernel(const La
     if (p.probs) {
         float* prow = p.probs + (int64_t)b * L;
 #pragma unroll
-        for (int t = 0; t < kLhPerLane; ++t) {
+        for (int t = 0; t < PER; ++t) {
             const int j = lane + 64 * t;
             if (j < L) prow[j] = fast_exp2(fmaf(z[t], kLog2eLh, -mc)) * inv;
         }
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(kLhWaves * kWave) void label_select_kernel(const La
         float best = -INFINITY;
         int bj = INT32_MAX;
 #pragma unroll
-        for (int t = 0; t < kLhPerLane; ++t) {
+        for (int t = 0; t < PER; ++t) {
             const int j = lane + 64 * t;
             if (j < L && !((taken >> t) & 1ull) && (z[t] > best || bj == INT32_MAX)) {
                 best = z[t];
@@ -148,8 +151,16 @@ hipError_t launch_label_head(const LabelHeadParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(label_logits_kernel, g1, dim3(kLhWaves * kWave), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(label_select_kernel, dim3((p.num_seqs + kLhWaves - 1) / kLhWaves), dim3(kLhWaves * kWave), 0,
-                       stream, p);
+    const dim3 g2((p.num_seqs + kLhWaves - 1) / kLhWaves), b2(kLhWaves * kWave);
+    const int per = (p.num_labels + kWave - 1) / kWave;     // num_labels <= kLabelMax
+    if (per <= 1)
+        hipLaunchKernelGGL(label_select_kernel<1>, g2, b2, 0, stream, p);
+    else if (per <= 4)
+        hipLaunchKernelGGL(label_select_kernel<4>, g2, b2, 0, stream, p);
+    else if (per <= 16)
+        hipLaunchKernelGGL(label_select_kernel<16>, g2, b2, 0, stream, p);
+    else
+        hipLaunchKernelGGL(label_select_kernel<kLhPerLane>, g2, b2, 0, stream, p);
     return hipGetLastError();
 }
 

@@ -71,8 +71,11 @@ def _check(got, hidden_bits, cu, lm_bits, labels, K, label_map=None, what=""):
     return exact
 
 
+# label counts cover every select variant (logits per lane 1, 4, 16 and 64, up to the 4,096 maximum)
 @pytest.mark.parametrize("lengths,H,V,L,K", [((3, 1, 7), 64, 100, 5, 2), ((9, 0, 4, 12, 0, 1), 128, 500, 33, 33),
-                                             ((5,) * 40, 256, 1000, 64, 5), ((2,) * 70, 1024, 3000, 300, 64)])
+                                             ((5,) * 40, 256, 1000, 64, 5), ((4,) * 9, 128, 2000, 200, 7),
+                                             ((2,) * 70, 1024, 3000, 300, 64), ((1,) * 5, 64, 5000, 1500, 10),
+                                             ((2, 3), 64, 8192, 4096, 3)])
 def test_shapes(gpu, lengths, H, V, L, K):
     note("label_head B=%d H=%d V=%d L=%d K=%d" % (len(lengths), H, V, L, K))
     rng = np.random.default_rng(sum(lengths) + H + L)
