@@ -37,8 +37,9 @@ def test_topk_tiny_workload(gpu):
     _eq(_topk(gpu, lp1, ref0[2], shape.width), oracle.topk_merge(lp1, ref0[2], shape.width), "step 1")
 
 
+# W = 256 and 257 are the two sides of the switch to the wide form (deeper pipeline, priority rotation)
 @pytest.mark.parametrize("R,Win,V,W", [(3, 1, 7, 7), (2, 3, 5, 15), (2, 5, 33, 40), (4, 7, 1003, 512),
-                                       (1, 64, 4096, 400), (2, 2, 9001, 1)])
+                                       (1, 64, 4096, 400), (2, 2, 9001, 1), (3, 9, 3001, 256), (3, 9, 3001, 257)])
 def test_topk_shapes_and_ties(gpu, R, Win, V, W):
     note("topk R=%d Win=%d V=%d W=%d tie stress" % (R, Win, V, W))
     rng = np.random.default_rng(R * 1000 + V)
