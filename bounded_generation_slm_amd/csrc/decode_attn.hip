@@ -328,20 +328,30 @@ __global__ __launch_bounds__(NTHR, (D == 64 ? 4 : 2)) void beam_decode_attn_kern
                 for (int e = 0; e < 4; ++e) part = dot2_bf16(qreg[ks][e], kv[ks][e], part);
             part = sum_halves(part);
             const float s = part * p.scale_log2;
-            const float mnew = fmaxf(mrun, s);     // finite: s is
-            const float alpha = fast_exp2(mrun - mnew);
-            const float pi = fast_exp2(s - mnew);
-            mrun = mnew;
-            lsum = lsum * alpha + (hf == 0 ? pi : 0.f);   // both halves hold the same score
+            // as in the prompt pass: the reference max may trail by up to
+            // kMaxLag, so O and the row sum are rescaled only when a row's
+            // score moves further (weights stay below 2^kMaxLag)
+            if (__ballot(s - mrun > kMaxLag) != 0) {
+                const float mnew = fmaxf(mrun, s);  // finite: s is
+                const float alpha = fast_exp2(mrun - mnew);
+                lsum *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+                mrun = mnew;
+            }
+            const float pi = fast_exp2(s - mrun);
+            lsum += hf == 0 ? pi : 0.f;             // both halves hold the same score
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4) {
                     const u32x2 x = vv[db * 4 + i4];
-                    o[db][4 * i4 + 0] = o[db][4 * i4 + 0] * alpha + pi * bf16_bits_to_f32(x[0] & 0xFFFFu);
-                    o[db][4 * i4 + 1] = o[db][4 * i4 + 1] * alpha + pi * bf16_bits_to_f32(x[0] >> 16);
-                    o[db][4 * i4 + 2] = o[db][4 * i4 + 2] * alpha + pi * bf16_bits_to_f32(x[1] & 0xFFFFu);
-                    o[db][4 * i4 + 3] = o[db][4 * i4 + 3] * alpha + pi * bf16_bits_to_f32(x[1] >> 16);
+                    o[db][4 * i4 + 0] = fmaf(pi, bf16_bits_to_f32(x[0] & 0xFFFFu), o[db][4 * i4 + 0]);
+                    o[db][4 * i4 + 1] = fmaf(pi, bf16_bits_to_f32(x[0] >> 16), o[db][4 * i4 + 1]);
+                    o[db][4 * i4 + 2] = fmaf(pi, bf16_bits_to_f32(x[1] & 0xFFFFu), o[db][4 * i4 + 2]);
+                    o[db][4 * i4 + 3] = fmaf(pi, bf16_bits_to_f32(x[1] >> 16), o[db][4 * i4 + 3]);
                 }
         }
 
