@@ -149,6 +149,7 @@ struct TopkParams {
     int64_t list_cap;                   // keys per request list
     int64_t seg;                        // candidates per stage-1 wave (a multiple of 4)
     int wpr, kslices;                   // sliced ranges: waves per request, slices per wave (0: contiguous)
+    bool deep;                          // stage 1 in the deep form (see beam_topk_deep)
     int num_requests, beams_in, vocab, width;
     // merge on logits only (logprobs then holds the logits):
     struct Piece {                      // one row's part of one stage-1 range
@@ -182,7 +183,18 @@ int beam_topk_logits_blocks_per_cu(int width);
 // at least kTopkMinRange, and few enough ranges per request for its list
 // (`lists` slots of W keys)
 int64_t beam_topk_segment(int num_requests, int beams_in, int vocab, int64_t resident_waves, int64_t lists);
-int beam_topk_blocks_per_cu(int width);     // resident stage-1 workgroups (4 waves) per CU
+// Stage 1 runs in one of two forms: four rounds of loads in flight per wave
+// at four workgroups per CU, or the deep form, eight rounds at three
+// workgroups per CU with each wave's issue priority rotated.  The deep form
+// serves widths above 256 (whose larger buffers need it) and calls of at
+// least kTopkDeepMin candidates at any width: over the short-prompt search's
+// merges (486M candidates, W = 100) it measured 4.6% faster, while calls of
+// 78M candidates were even or up to 3.6% slower and the search's first
+// merge (4.9M) 7% slower: the deeper pipeline pays on long streams, more
+// waves on short ones.
+constexpr int64_t kTopkDeepMin = (int64_t)1 << 27;
+bool beam_topk_deep(int width, int64_t candidates);
+int beam_topk_blocks_per_cu(int width, bool deep);   // resident stage-1 workgroups (4 waves) per CU
 // Shortest stage-1 range of the merge on log-probs (first merges, one beam
 // per request, measured best at 2,048: 1,024 tied at 8 x 400 beams and ran
 // 4% slower at 32 x 100, 4,096 ran 10-35% slower)

@@ -34,7 +34,7 @@ struct slm_ctx {
     int plan_cap = 0;
     int num_cus = 256;
     size_t max_lds = 0;
-    int topk_blocks_per_cu[slm::kTopkMaxWidth + 1] = {0};   // stage-1 occupancy per width (0 = not queried)
+    int topk_blocks_per_cu[2][slm::kTopkMaxWidth + 1] = {};   // stage-1 occupancy per [deep form][width] (0 = not queried)
     int topk_logits_blocks_per_cu[slm::kTopkMaxWidth + 1] = {0};   // the same, merge on logits
     slm::LaunchCache launch_cache;  // occupancy and LDS limits of the attention kernels on this device
     // the current prefill plan: the pack its work list was built for, and its id
@@ -523,11 +523,12 @@ slm_status slm_beam_topk_merge(slm_ctx* ctx, const float* logprobs, const float*
     p.num_requests = num_requests; p.beams_in = beams_in; p.vocab = vocab; p.width = width;
     // stage-1 waves take equal ranges of the flattened candidates, one per
     // resident wave (four waves per workgroup)
-    int bpc = ctx->topk_blocks_per_cu[width];
+    p.deep = slm::beam_topk_deep(width, (int64_t)num_requests * beams_in * vocab);
+    int bpc = ctx->topk_blocks_per_cu[p.deep][width];
     if (bpc == 0) {
         const bool query = !ctx->dry_run && !ctx->validating;
-        bpc = query ? slm::beam_topk_blocks_per_cu(width) : 1;
-        if (query) ctx->topk_blocks_per_cu[width] = bpc;
+        bpc = query ? slm::beam_topk_blocks_per_cu(width, p.deep) : 1;
+        if (query) ctx->topk_blocks_per_cu[p.deep][width] = bpc;
     }
     const int64_t resident = (int64_t)ctx->num_cus * bpc * 4;
     p.seg = slm::beam_topk_segment(num_requests, beams_in, vocab, resident, ctx->topk_lists);

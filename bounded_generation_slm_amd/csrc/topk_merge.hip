@@ -307,10 +307,11 @@ __device__ __forceinline__ uint64_t* req_slot(const TopkParams& p, int r, int s)
 constexpr int kWLanes = 64;
 constexpr int kWPerLane = 8;                        // candidates per lane per round
 constexpr int kWRound = kWLanes * kWPerLane;        // 512
-// Rounds in flight per wave: 4 where four workgroups share a CU (W <= 256),
-// 8 where the wider buffers leave room for three (their registers allow it,
-// and fewer waves each need more bytes in flight).
-__host__ __device__ constexpr int stream_depth(bool wide) { return wide ? 8 : 4; }
+// Rounds in flight per wave: 4 where four workgroups share a CU, 8 in the
+// deep form at three (its registers allow it, and fewer waves each need more
+// bytes in flight); the deep form serves W > 256, whose wider buffers leave
+// room for three workgroups only, and long calls (beam_topk_deep).
+__host__ __device__ constexpr int stream_depth(bool deep) { return deep ? 8 : 4; }
 __host__ __device__ inline bool wide_width(int W) { return W > kWRound / 2; }
 constexpr int kWDepth = 4;                          // the merge on logits: rounds in flight
 constexpr int kWBins = 256;
@@ -642,13 +643,13 @@ __global__ __launch_bounds__(kTkThreads, (DEPTH == stream_depth(false) ? 4 : 3))
     };
 
     constexpr int NV = kWPerLane / 4;
-    // Wide widths run three workgroups per CU, and under oldest-first issue
+    // The deep form runs three workgroups per CU, and under oldest-first issue
     // arbitration the workgroups dispatched later to a CU streamed ~15% slower,
     // so the call ended with them.  There each wave steps its issue priority
     // through the four levels, one per group of DEPTH rounds, starting from its
     // index mod 4, so no wave stays behind the others for long.  (At four
-    // workgroups per CU the rotation measured slightly slower; those keep the
-    // default priority.)
+    // workgroups per CU the rotation measured slightly slower; that form keeps
+    // the default priority.)
     constexpr bool rotate = DEPTH > stream_depth(false);
     int prio = (int)(wid & 3);
     for (int si = 0;;) {
@@ -1186,9 +1187,8 @@ hipError_t launch_beam_topk_merge(const TopkParams& p, hipStream_t stream) {
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const size_t lds = beam_topk_stage1_lds(p.width);
     constexpr int D4 = stream_depth(false), D8 = stream_depth(true);
-    const bool wide = wide_width(p.width);
-    auto kern = vec ? (wide ? topk_stage1_kernel<true, D8> : topk_stage1_kernel<true, D4>)
-                    : (wide ? topk_stage1_kernel<false, D8> : topk_stage1_kernel<false, D4>);
+    auto kern = vec ? (p.deep ? topk_stage1_kernel<true, D8> : topk_stage1_kernel<true, D4>)
+                    : (p.deep ? topk_stage1_kernel<false, D8> : topk_stage1_kernel<false, D4>);
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kTkThreads), lds, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1282,11 +1282,13 @@ int beam_topk_logits_blocks_per_cu(int width) {
     return n;
 }
 
-int beam_topk_blocks_per_cu(int width) {
+bool beam_topk_deep(int width, int64_t candidates) { return wide_width(width) || candidates >= kTopkDeepMin; }
+
+int beam_topk_blocks_per_cu(int width, bool deep) {
     int n = 0;
     const size_t lds = beam_topk_stage1_lds(width);
-    const void* kern = wide_width(width) ? (const void*)topk_stage1_kernel<true, stream_depth(true)>
-                                         : (const void*)topk_stage1_kernel<true, stream_depth(false)>;
+    const void* kern = deep ? (const void*)topk_stage1_kernel<true, stream_depth(true)>
+                            : (const void*)topk_stage1_kernel<true, stream_depth(false)>;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kTkThreads, lds) !=
             hipSuccess || n <= 0)
         n = 1;
